@@ -1,0 +1,148 @@
+"""Bookkeeping model of the fused all-gather + GEMM (TEST INFRASTRUCTURE ONLY).
+
+The method (ROCm/iris issue "Fused all-gather+GEMM HBM-buffer kernel for iris.ops",
+opening summary): workgroups split into fetchers and GEMM workers; fetchers copy A tiles
+into a local staging buffer and set one ready flag per tile; GEMM workers wait on those
+flags and compute as tiles arrive. Tiles of the local shard are read in place and never
+staged (pytorch/helion PR "[Benchmark] Add all gather matmul benchmark", the Kraken
+optimization comment). Flag granularity is one flag per (m-tile, group of k_per_flag
+K-tiles), after the k_per_flag tunable in the iris issue's defaults table.
+
+This module restates, independently of the GPU library, the static schedule that the GPU
+library documents, so that its debug logs, flag array and staging buffer can be checked
+bit for bit:
+
+  T_m = ceil(M/BM), T_n = ceil(N/BN), KG = k_per_flag*BK, G = ceil(K/KG)
+  owner(t)   = (t*BM) // M_s                         shard of the m-tile's first row
+  direct(t)  = direct_local and the whole m-tile lies inside shard `rank`
+  S          = direct m-tiles ascending, then the others by ((owner - rank) mod D, t)
+  tile q     = (S[q // T_n], q % T_n)                GEMM order, n fastest
+  staged S'  = [t in S if not direct(t)]
+  units      = for each window of Wm = max(1, ceil(W / T_n)) consecutive entries of S':
+                 for g in 0..G-1: for t in window: (t, g)
+  unit u  -> fetcher u mod F, each fetcher in increasing u
+  flags[t*G + g] == epoch after a run, for every staged unit; direct units untouched
+  staging, k_contiguous:  S[m*K + k] = A[m][k];  m_contiguous: S[k*M + m] = A[m][k]
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    D: int
+    M: int
+    N: int
+    K: int
+    BM: int
+    BN: int
+    BK: int
+    k_per_flag: int
+    rank: int
+    direct_local: bool
+    F: int          # fetcher workgroups (may be 0 when nothing is staged)
+    W: int          # workgroups in the grid (fetchers included)
+
+    @property
+    def M_s(self) -> int:
+        return self.M // self.D
+
+    @property
+    def T_m(self) -> int:
+        return -(-self.M // self.BM)
+
+    @property
+    def T_n(self) -> int:
+        return -(-self.N // self.BN)
+
+    @property
+    def KG(self) -> int:
+        return self.k_per_flag * self.BK
+
+    @property
+    def G(self) -> int:
+        return -(-self.K // self.KG) if self.K > 0 else 0
+
+
+def owner(g: Geometry, t: int) -> int:
+    return (t * g.BM) // g.M_s
+
+
+def is_direct(g: Geometry, t: int) -> bool:
+    if not g.direct_local:
+        return False
+    lo = t * g.BM
+    hi = min(g.M, (t + 1) * g.BM)
+    return g.rank * g.M_s <= lo and hi <= (g.rank + 1) * g.M_s
+
+
+def mtile_order(g: Geometry) -> List[int]:
+    direct = [t for t in range(g.T_m) if is_direct(g, t)]
+    other = [t for t in range(g.T_m) if not is_direct(g, t)]
+    other.sort(key=lambda t: ((owner(g, t) - g.rank) % g.D, t))
+    return direct + other
+
+
+def gemm_tiles(g: Geometry) -> List[Tuple[int, int]]:
+    """Tile q -> (t_m, t_n) in GEMM order."""
+    return [(t, n) for t in mtile_order(g) for n in range(g.T_n)]
+
+
+def fetch_units(g: Geometry) -> List[Tuple[int, int]]:
+    """Unit u -> (t_m, k-group) in fetch order."""
+    staged = [t for t in mtile_order(g) if not is_direct(g, t)]
+    wm = max(1, -(-g.W // max(1, g.T_n)))
+    units = []
+    for ws in range(0, len(staged), wm):
+        win = staged[ws:ws + wm]
+        for kg in range(g.G):
+            for t in win:
+                units.append((t, kg))
+    return units
+
+
+def fetcher_lists(g: Geometry) -> List[List[int]]:
+    """For each fetcher f, the unit indices it copies, in order."""
+    n = len(fetch_units(g))
+    if g.F == 0:
+        assert n == 0
+        return []
+    return [list(range(f, n, g.F)) for f in range(g.F)]
+
+
+def expected_flags(g: Geometry, epoch: int, prior: np.ndarray = None) -> np.ndarray:
+    """Flag array [T_m * G] after a run with the given epoch."""
+    size = g.T_m * g.G
+    flags = np.zeros(size, dtype=np.uint32) if prior is None else prior.astype(np.uint32).copy()
+    for (t, kg) in fetch_units(g):
+        flags[t * g.G + kg] = epoch
+    return flags
+
+
+def staged_rows(g: Geometry) -> np.ndarray:
+    """Boolean mask over the M rows of A: True where the row is staged."""
+    mask = np.zeros(g.M, dtype=bool)
+    for t in range(g.T_m):
+        if not is_direct(g, t):
+            mask[t * g.BM:min(g.M, (t + 1) * g.BM)] = True
+    return mask
+
+
+def expected_staging(g: Geometry, A_bits: np.ndarray, layout: str, poison: int) -> np.ndarray:
+    """Staging buffer contents (uint16) after a run that started from `poison` everywhere."""
+    assert A_bits.shape == (g.M, g.K)
+    mask = staged_rows(g)
+    if layout == "k_contiguous":
+        st = np.full((g.M, g.K), poison, dtype=np.uint16)
+        st[mask, :] = A_bits[mask, :]
+        return st.reshape(-1)
+    if layout == "m_contiguous":
+        st = np.full((g.K, g.M), poison, dtype=np.uint16)
+        st[:, mask] = A_bits[mask, :].T
+        return st.reshape(-1)
+    raise ValueError(layout)

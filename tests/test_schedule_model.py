@@ -1,0 +1,98 @@
+"""Pins of the bookkeeping model (oracle/schedule_model.py) on small hand-checked cases
+and on invariants that any correct schedule must satisfy: every staged unit fetched
+exactly once, every output tile computed exactly once, local-shard m-tiles never staged,
+the local shard's m-tiles first in GEMM order, shards visited in rank-rotated order."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import schedule_model as sm
+
+
+def geo(**kw):
+    base = dict(D=2, M=4, N=4, K=4, BM=2, BN=2, BK=1, k_per_flag=2, rank=0, direct_local=True,
+                F=2, W=4)
+    base.update(kw)
+    return sm.Geometry(**base)
+
+
+def test_hand_example_two_shards():
+    g = geo()
+    assert (g.T_m, g.T_n, g.G) == (2, 2, 2)
+    assert [sm.is_direct(g, t) for t in range(2)] == [True, False]
+    assert sm.gemm_tiles(g) == [(0, 0), (0, 1), (1, 0), (1, 1)]
+    assert sm.fetch_units(g) == [(1, 0), (1, 1)]
+    assert sm.fetcher_lists(g) == [[0], [1]]
+    assert list(sm.expected_flags(g, 7)) == [0, 0, 7, 7]
+
+
+def test_hand_example_rank_rotation_and_straddle():
+    # D=2, M_s=3, BM=2: m-tile 1 (rows 2,3) straddles shards 0 and 1
+    g = geo(M=6, rank=1, N=2, BN=2)
+    assert [sm.owner(g, t) for t in range(3)] == [0, 0, 1]
+    assert [sm.is_direct(g, t) for t in range(3)] == [False, False, True]
+    # own (direct) m-tile 2 first, then shard rank+1 = 0: m-tiles 0 and 1
+    assert sm.mtile_order(g) == [2, 0, 1]
+    # W=4, T_n=1 -> window of 4 m-tiles; k-groups outer inside the window
+    assert sm.fetch_units(g) == [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+def test_hand_example_four_shards_rank2():
+    g = geo(D=4, M=8, BM=2, rank=2, N=2, BN=2, W=2, F=1, K=2, k_per_flag=2)
+    # shards: 0 -> t0, 1 -> t1, 2 -> t2 (own), 3 -> t3
+    assert sm.mtile_order(g) == [2, 3, 0, 1]
+    assert sm.fetch_units(g) == [(3, 0), (0, 0), (1, 0)]   # window of 2: [3, 0], then [1]
+
+
+def test_direct_local_off_stages_everything():
+    g = geo(direct_local=False)
+    assert sorted(sm.fetch_units(g)) == [(0, 0), (0, 1), (1, 0), (1, 1)]
+    assert sm.staged_rows(g).all()
+
+
+@pytest.mark.parametrize("D,M,N,K,BM,BN,BK,kpf,rank,dl,F,W", [
+    (8, 1024, 1024, 1024, 128, 128, 64, 4, 0, True, 8, 64),
+    (4, 4096, 3584, 8192, 256, 256, 64, 16, 3, True, 32, 256),
+    (8, 16384, 3584, 8192, 256, 256, 64, 16, 5, True, 32, 256),
+    (3, 300, 200, 130, 64, 64, 64, 1, 1, True, 3, 10),        # ragged everything
+    (5, 35, 17, 9, 16, 16, 8, 2, 4, False, 2, 3),
+    (1, 64, 64, 64, 32, 32, 32, 1, 0, True, 0, 4),             # D=1: nothing staged
+])
+def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
+    g = sm.Geometry(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W)
+    tiles = sm.gemm_tiles(g)
+    assert sorted(tiles) == sorted(itertools.product(range(g.T_m), range(g.T_n)))
+    units = sm.fetch_units(g)
+    assert len(set(units)) == len(units)
+    staged = {t for t in range(g.T_m) if not sm.is_direct(g, t)}
+    assert set(units) == set(itertools.product(sorted(staged), range(g.G)))
+    # local-shard m-tiles come first in GEMM order
+    order = sm.mtile_order(g)
+    nd = sum(sm.is_direct(g, t) for t in range(g.T_m))
+    assert all(sm.is_direct(g, t) for t in order[:nd])
+    # rank-rotated shard order among the rest
+    keys = [(sm.owner(g, t) - rank) % D for t in order[nd:]]
+    assert keys == sorted(keys)
+    # fetcher lists partition the units
+    if units:
+        lists = sm.fetcher_lists(g)
+        assert sorted(itertools.chain(*lists)) == list(range(len(units)))
+        assert all(lst == sorted(lst) for lst in lists)
+    # flags: exactly the staged units carry the epoch
+    f = sm.expected_flags(g, 5)
+    assert int((f == 5).sum()) == len(units)
+    # a k-group is fetched no later than the next k-group of the same m-tile
+    pos = {u: i for i, u in enumerate(units)}
+    for (t, kg), i in pos.items():
+        if kg + 1 < g.G:
+            assert pos[(t, kg + 1)] > i
+
+
+def test_expected_staging_layouts():
+    g = geo(D=2, M=4, K=3, BM=2)
+    A = np.arange(12, dtype=np.uint16).reshape(4, 3) + 100
+    k = sm.expected_staging(g, A, "k_contiguous", 0xFFFF).reshape(4, 3)
+    assert (k[:2] == 0xFFFF).all() and (k[2:] == A[2:]).all()
+    m = sm.expected_staging(g, A, "m_contiguous", 0xFFFF).reshape(3, 4)
+    assert (m[:, :2] == 0xFFFF).all() and (m[:, 2:] == A[2:].T).all()
