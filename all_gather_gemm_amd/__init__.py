@@ -1,0 +1,271 @@
+"""Fused all-gather + GEMM for AMD MI355X (gfx950): Python binding of libagmm.so.
+
+out[M, N] = concat(shard_0, ..., shard_{D-1}) @ B (+ bias), computed by hand-written gfx950
+HIP kernels behind the C ABI in include/agmm.h. This module only marshals arguments: it
+builds the descriptor struct, passes device pointers and the current HIP stream, and turns
+error codes into exceptions. Every step of the computation runs in the library's kernels;
+there is no fallback path. If libagmm.so is missing, importing this module raises.
+
+The functions mirror the C names: ag_matmul_desc_init, ag_matmul_create, ag_matmul_run,
+ag_matmul_destroy, ag_matmul_workspace_bytes, ag_matmul_strerror, ag_matmul_get_config,
+ag_matmul_debug_query, ag_matmul_debug_fill_staging. `AgMatmul` wraps a handle for torch
+tensors (data pointers and torch's current stream only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libagmm.so")
+
+AGMM_MAX_SHARDS = 64
+AGMM_OK = 0
+ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "OOM", -5: "TIMEOUT",
+          -6: "WRONG_DEVICE", -7: "POISONED"}
+F16, BF16 = 0, 1
+K_CONTIGUOUS, M_CONTIGUOUS = 0, 1
+ALGO_FUSED, ALGO_BASELINE = 0, 1
+Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES = 1, 2, 3, 4, 5, 6, 7
+EV_FETCH, EV_GEMM, EV_GEMM_WAIT = 1, 2, 3
+
+EXPORTED = [
+    "ag_matmul_desc_init", "ag_matmul_create", "ag_matmul_run", "ag_matmul_destroy",
+    "ag_matmul_workspace_bytes", "ag_matmul_strerror", "ag_matmul_last_hip_error",
+    "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
+]
+
+
+class agmm_desc(ctypes.Structure):
+    _fields_ = [
+        ("D", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32), ("algo", ctypes.c_int32),
+        ("direct_local", ctypes.c_int32), ("has_bias", ctypes.c_int32), ("debug", ctypes.c_int32),
+        ("block_m", ctypes.c_int32), ("k_per_flag", ctypes.c_int32),
+        ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
+        ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
+        ("debug_skip_unit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+class agmm_config(ctypes.Structure):
+    _fields_ = [
+        ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("k_per_flag", ctypes.c_int32), ("T_m", ctypes.c_int32), ("T_n", ctypes.c_int32),
+        ("G", ctypes.c_int32), ("num_units", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
+        ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
+        ("num_copy_wgs", ctypes.c_int32), ("trace_cap", ctypes.c_int32),
+        ("epoch", ctypes.c_uint32), ("staging_elems", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class agmm_trace_rec(ctypes.Structure):
+    _fields_ = [("event", ctypes.c_uint32), ("id", ctypes.c_uint32), ("a", ctypes.c_uint32),
+                ("b", ctypes.c_uint32), ("t0", ctypes.c_uint64), ("t1", ctypes.c_uint64)]
+
+
+TRACE_DTYPE = np.dtype([("event", "<u4"), ("id", "<u4"), ("a", "<u4"), ("b", "<u4"),
+                        ("t0", "<u8"), ("t1", "<u8")])
+
+
+class AgmmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERRORS.get(code, code)} ({strerror(code)})"
+                         + (f", hipError {last_hip_error()}" if code == -3 else ""))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run all_gather_gemm_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.ag_matmul_desc_init.argtypes = [ctypes.POINTER(agmm_desc)]
+    lib.ag_matmul_desc_init.restype = None
+    lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp)]
+    lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.ag_matmul_destroy.argtypes = [vp]
+    lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
+    lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
+    lib.ag_matmul_strerror.argtypes = [ctypes.c_int]
+    lib.ag_matmul_strerror.restype = ctypes.c_char_p
+    lib.ag_matmul_last_hip_error.restype = ctypes.c_int
+    lib.ag_matmul_get_config.argtypes = [vp, ctypes.POINTER(agmm_config)]
+    lib.ag_matmul_debug_query.argtypes = [vp, ctypes.c_int, vp, ctypes.c_size_t]
+    lib.ag_matmul_debug_fill_staging.argtypes = [vp, ctypes.c_uint16, vp]
+    return lib
+
+
+lib = _load()
+
+
+# ---- C-named functions (argument marshalling only) ----
+
+def ag_matmul_desc_init(**fields) -> agmm_desc:
+    d = agmm_desc()
+    lib.ag_matmul_desc_init(ctypes.byref(d))
+    for k, v in fields.items():
+        if not hasattr(d, k):
+            raise AttributeError(f"agmm_desc has no field {k!r}")
+        setattr(d, k, int(v))
+    return d
+
+
+def ag_matmul_create(desc: agmm_desc) -> int:
+    h = ctypes.c_void_p()
+    rc = lib.ag_matmul_create(ctypes.byref(desc), ctypes.byref(h))
+    if rc != AGMM_OK:
+        raise AgmmError(rc, "ag_matmul_create")
+    return h.value
+
+
+def ag_matmul_run(handle: int, shard_ptrs: Sequence[int], B_ptr: int, bias_ptr: Optional[int],
+                  out_ptr: int, stream: int = 0) -> int:
+    arr = (ctypes.c_void_p * max(1, len(shard_ptrs)))(*[ctypes.c_void_p(p) for p in shard_ptrs])
+    return lib.ag_matmul_run(ctypes.c_void_p(handle), arr, ctypes.c_void_p(B_ptr),
+                             ctypes.c_void_p(bias_ptr) if bias_ptr else None,
+                             ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
+
+
+def ag_matmul_destroy(handle: Optional[int]) -> int:
+    return lib.ag_matmul_destroy(ctypes.c_void_p(handle) if handle else None)
+
+
+def ag_matmul_workspace_bytes(desc: agmm_desc) -> int:
+    return int(lib.ag_matmul_workspace_bytes(ctypes.byref(desc)))
+
+
+def strerror(code: int) -> str:
+    return lib.ag_matmul_strerror(code).decode()
+
+
+ag_matmul_strerror = strerror
+
+
+def last_hip_error() -> int:
+    return int(lib.ag_matmul_last_hip_error())
+
+
+def ag_matmul_get_config(handle: int) -> agmm_config:
+    c = agmm_config()
+    rc = lib.ag_matmul_get_config(ctypes.c_void_p(handle), ctypes.byref(c))
+    if rc != AGMM_OK:
+        raise AgmmError(rc, "ag_matmul_get_config")
+    return c
+
+
+def ag_matmul_debug_query(handle: int, what: int, nbytes: int) -> bytes:
+    buf = (ctypes.c_uint8 * max(1, nbytes))()
+    rc = lib.ag_matmul_debug_query(ctypes.c_void_p(handle), what, buf, nbytes)
+    if rc != AGMM_OK:
+        raise AgmmError(rc, "ag_matmul_debug_query")
+    return bytes(buf)[:nbytes]
+
+
+def ag_matmul_debug_fill_staging(handle: int, pattern: int, stream: int = 0) -> int:
+    return lib.ag_matmul_debug_fill_staging(ctypes.c_void_p(handle), pattern & 0xFFFF,
+                                            ctypes.c_void_p(stream))
+
+
+# ---- torch convenience wrapper (pointers and the current stream only) ----
+
+class AgMatmul:
+    """One handle for one problem shape. run() takes D shard tensors [M/D, K], B [K, N],
+    an optional bias [N] and an output [M, N], all contiguous on the handle's device."""
+
+    def __init__(self, D: int, M: int, N: int, K: int, dtype="f16", layout="k_contiguous",
+                 algo="fused", rank: int = 0, direct_local: bool = True, has_bias: bool = False,
+                 debug: bool = False, **tunables):
+        self.desc = ag_matmul_desc_init(
+            D=D, M=M, N=N, K=K, rank=rank,
+            dtype={"f16": F16, "bf16": BF16}[dtype],
+            layout={"k_contiguous": K_CONTIGUOUS, "m_contiguous": M_CONTIGUOUS}[layout],
+            algo={"fused": ALGO_FUSED, "baseline": ALGO_BASELINE}[algo],
+            direct_local=int(direct_local), has_bias=int(has_bias), debug=int(debug), **tunables)
+        self.dtype = dtype
+        self.handle = ag_matmul_create(self.desc)
+        self.config = ag_matmul_get_config(self.handle)
+
+    def close(self):
+        if self.handle:
+            ag_matmul_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def run(self, shards, B, bias=None, out=None, stream=None, check: bool = True):
+        import torch
+        d = self.desc
+        if len(shards) != d.D:
+            raise ValueError(f"expected {d.D} shards, got {len(shards)}")
+        tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        for t in list(shards) + [B] + ([bias] if bias is not None else []):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors of the handle's dtype")
+        if out is None:
+            out = torch.empty((d.M, d.N), dtype=tdt, device=B.device)
+        s = stream if stream is not None else torch.cuda.current_stream(B.device)
+        rc = ag_matmul_run(self.handle, [t.data_ptr() for t in shards], B.data_ptr(),
+                           bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                           s.cuda_stream)
+        if check and rc != AGMM_OK:
+            raise AgmmError(rc, "ag_matmul_run")
+        return out
+
+    # ---- bookkeeping access ----
+    def flags(self) -> np.ndarray:
+        c = self.config
+        n = c.T_m * c.G
+        return np.frombuffer(ag_matmul_debug_query(self.handle, Q_FLAGS, n * 4), dtype="<u4")
+
+    def staging(self) -> np.ndarray:
+        n = self.config.staging_elems
+        return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STAGING, n * 2), dtype="<u2")
+
+    def units(self) -> np.ndarray:
+        n = self.config.num_units
+        return np.frombuffer(ag_matmul_debug_query(self.handle, Q_UNITS, n * 8),
+                             dtype="<u4").reshape(-1, 2)
+
+    def mtiles(self) -> np.ndarray:
+        n = self.config.T_m
+        return np.frombuffer(ag_matmul_debug_query(self.handle, Q_MTILES, n * 4), dtype="<u4")
+
+    def status(self) -> np.ndarray:
+        return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STATUS, 16), dtype="<u4")
+
+    def trace(self):
+        c = self.config
+        W = c.num_wgs
+        counts = np.frombuffer(ag_matmul_debug_query(self.handle, Q_TRACE_COUNT, W * 4), dtype="<u4")
+        recs = np.frombuffer(ag_matmul_debug_query(self.handle, Q_TRACE,
+                                                   W * c.trace_cap * TRACE_DTYPE.itemsize),
+                             dtype=TRACE_DTYPE).reshape(W, c.trace_cap)
+        return counts, recs
+
+    def fill_staging(self, pattern: int, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = ag_matmul_debug_fill_staging(self.handle, pattern, s.cuda_stream)
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_matmul_debug_fill_staging")

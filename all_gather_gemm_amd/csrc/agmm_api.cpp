@@ -1,0 +1,455 @@
+// Host side of the C ABI declared in include/agmm.h: validation, tile-configuration
+// choice, schedule tables, workspace, launch.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "agmm_internal.h"
+
+using agmm::KParams;
+
+struct agmm_handle {
+  agmm_desc desc;
+  agmm_config cfg;
+  int64_t M_s;
+  char* ws;                 // one device allocation, carved below
+  uint16_t* staging;
+  uint32_t* flags;
+  uint32_t* ctr;
+  uint32_t* units;
+  uint32_t* mtiles;
+  agmm_trace_rec* trace;
+  uint32_t* trace_count;
+  int64_t flags_n;
+  int64_t trace_wgs;        // workgroups the trace buffer has room for
+  std::vector<uint32_t> h_units, h_mtiles;
+  bool poisoned;
+};
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// Per-thread byte offsets inside a tile are 32-bit: 256 rows of a 2^23-element stride fit.
+constexpr int64_t kMaxDim = (int64_t)1 << 23;
+constexpr int64_t kMaxCount = (int64_t)1 << 31;
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // ~ several seconds of backed-off polls
+constexpr int kDefaultTraceCap = 512;
+constexpr int kTraceWgsAuto = 2048;
+constexpr int kDefaultFetchWgs = 32;  // the iris issue's tuned num_fetch_sms default
+
+#define AGMM_HIP(x)                      \
+  do {                                   \
+    hipError_t e_ = (x);                 \
+    if (e_ != hipSuccess) {              \
+      g_last_hip = (int)e_;              \
+      return AGMM_ERR_HIP;               \
+    }                                    \
+  } while (0)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+int validate_desc(const agmm_desc* d) {
+  if (!d) return AGMM_ERR_INVALID_ARG;
+  if (d->D < 1 || d->D > AGMM_MAX_SHARDS) return AGMM_ERR_INVALID_ARG;
+  if (d->rank < 0 || d->rank >= d->D) return AGMM_ERR_INVALID_ARG;
+  if (d->M < 0 || d->N < 0 || d->K < 0) return AGMM_ERR_INVALID_ARG;
+  if (d->M >= kMaxDim || d->N >= kMaxDim || d->K >= kMaxDim) return AGMM_ERR_UNSUPPORTED;
+  if (d->M % d->D != 0) return AGMM_ERR_INVALID_ARG;
+  if (d->dtype != AGMM_F16 && d->dtype != AGMM_BF16) return AGMM_ERR_INVALID_ARG;
+  if (d->layout != AGMM_K_CONTIGUOUS && d->layout != AGMM_M_CONTIGUOUS) return AGMM_ERR_INVALID_ARG;
+  if (d->algo != AGMM_ALGO_FUSED && d->algo != AGMM_ALGO_BASELINE) return AGMM_ERR_INVALID_ARG;
+  if ((d->direct_local | d->has_bias | d->debug) & ~1) return AGMM_ERR_INVALID_ARG;
+  if (d->block_m != 0 && d->block_m != 64 && d->block_m != 128 && d->block_m != 256)
+    return AGMM_ERR_INVALID_ARG;
+  if (d->k_per_flag < 0 || d->num_fetch_wgs < 0 || d->num_wgs < 0 || d->trace_cap < 0)
+    return AGMM_ERR_INVALID_ARG;
+  if (d->debug_skip_unit < -1) return AGMM_ERR_INVALID_ARG;
+  if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
+  if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
+    return AGMM_ERR_UNSUPPORTED;
+  return AGMM_OK;
+}
+
+bool is_direct(const agmm_desc& d, int64_t M_s, int bm, int64_t t) {
+  if (!d.direct_local) return false;
+  const int64_t lo = t * bm, hi = std::min(d.M, (t + 1) * bm);
+  return (int64_t)d.rank * M_s <= lo && hi <= (int64_t)(d.rank + 1) * M_s;
+}
+
+// Everything create decides, computed on the host only.
+struct Plan {
+  agmm_config cfg;
+  int64_t M_s;
+  std::vector<uint32_t> units, mtiles;
+  int64_t flags_n, trace_wgs;
+  int64_t off_staging, off_flags, off_ctr, off_units, off_mtiles, off_trace, off_tcount, total;
+};
+
+int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
+  agmm_config& c = pl->cfg;
+  memset(&c, 0, sizeof(c));
+  const int64_t M_s = d.M / d.D;
+  pl->M_s = M_s;
+  c.num_cus = num_cus;
+
+  // Tile family: the largest square tile that still gives most CUs a tile.
+  int bm = d.block_m;
+  if (bm == 0) {
+    bm = 64;
+    for (int cand : {256, 128}) {
+      if (cdiv(d.M, cand) * cdiv(d.N, cand) * 4 >= (int64_t)num_cus * 3) {
+        bm = cand;
+        break;
+      }
+    }
+  }
+  c.block_m = c.block_n = bm;
+  c.block_k = 16384 / bm;
+  c.k_per_flag = d.k_per_flag ? d.k_per_flag : std::max(1, 1024 / c.block_k);
+  const int64_t KG = (int64_t)c.k_per_flag * c.block_k;
+  const int64_t T_m = cdiv(d.M, bm), T_n = cdiv(d.N, bm);
+  const int64_t G = d.K > 0 ? cdiv(d.K, KG) : 0;
+  if (T_m * T_n >= kMaxCount || T_m * G >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
+  c.T_m = (int32_t)T_m;
+  c.T_n = (int32_t)T_n;
+  c.G = (int32_t)G;
+  c.num_tiles = (int32_t)(T_m * T_n);
+
+  // GEMM order of m-tiles: in-place (local-shard) tiles first, then the others by shard in
+  // rank-rotated order (rank+1, rank+2, ...), ascending within a shard.
+  std::vector<int64_t> direct, other;
+  for (int64_t t = 0; t < T_m; ++t) (is_direct(d, M_s, bm, t) ? direct : other).push_back(t);
+  std::stable_sort(other.begin(), other.end(), [&](int64_t a, int64_t b) {
+    const int64_t ka = ((a * bm) / M_s - d.rank + d.D) % d.D;
+    const int64_t kb = ((b * bm) / M_s - d.rank + d.D) % d.D;
+    return ka < kb;
+  });
+  pl->mtiles.clear();
+  for (int64_t t : direct) pl->mtiles.push_back((uint32_t)t | 0x80000000u);
+  for (int64_t t : other) pl->mtiles.push_back((uint32_t)t);
+
+  const int64_t n_units = (int64_t)other.size() * G;
+  if (n_units >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
+  c.num_units = (int32_t)n_units;
+
+  // Grid: one workgroup per CU (a 128 KiB LDS footprint allows one), fetchers first.
+  int F = 0;
+  if (n_units > 0) F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
+  F = (int)std::min<int64_t>(F, n_units);
+  int64_t W = d.num_wgs ? d.num_wgs : num_cus;
+  W = std::min<int64_t>(W, num_cus);                  // every workgroup resident
+  W = std::min<int64_t>(W, (int64_t)F + c.num_tiles);  // no idle workgroups
+  F = (int)std::min<int64_t>(F, W);
+  if (c.num_tiles > 0 && W < 1) W = 1;
+  c.num_fetch_wgs = F;
+  c.num_wgs = (int32_t)W;
+  c.num_copy_wgs = (int32_t)std::min<int64_t>(n_units, 4LL * num_cus);
+
+  // Fetch order: staged m-tiles in GEMM order, in windows of the m-tiles the grid works on
+  // at once; inside a window, k-group by k-group.
+  pl->units.clear();
+  const int64_t wm = std::max<int64_t>(1, cdiv(W, std::max<int64_t>(1, T_n)));
+  for (size_t ws = 0; ws < other.size(); ws += (size_t)wm) {
+    const size_t we = std::min(other.size(), ws + (size_t)wm);
+    for (int64_t g = 0; g < G; ++g)
+      for (size_t i = ws; i < we; ++i) {
+        pl->units.push_back((uint32_t)other[i]);
+        pl->units.push_back((uint32_t)g);
+      }
+  }
+
+  c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
+  pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
+  c.staging_elems = n_units > 0 ? d.M * d.K : 0;
+  pl->flags_n = std::max<int64_t>(1, T_m * G);
+
+  int64_t off = 0;
+  pl->off_staging = off; off = align256(off + c.staging_elems * 2);
+  pl->off_flags = off;   off = align256(off + pl->flags_n * 4);
+  pl->off_ctr = off;     off = align256(off + agmm::CTR_WORDS * 4);
+  pl->off_units = off;   off = align256(off + std::max<int64_t>(1, n_units) * 8);
+  pl->off_mtiles = off;  off = align256(off + std::max<int64_t>(1, T_m) * 4);
+  pl->off_trace = off;   off = align256(off + pl->trace_wgs * c.trace_cap * (int64_t)sizeof(agmm_trace_rec));
+  pl->off_tcount = off;  off = align256(off + std::max<int64_t>(1, pl->trace_wgs) * 4);
+  pl->total = off;
+  c.workspace_bytes = off;
+  return AGMM_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+}  // namespace
+
+extern "C" {
+
+void ag_matmul_desc_init(agmm_desc* d) {
+  if (!d) return;
+  memset(d, 0, sizeof(*d));
+  d->D = 1;
+  d->dtype = AGMM_F16;
+  d->layout = AGMM_K_CONTIGUOUS;
+  d->algo = AGMM_ALGO_FUSED;
+  d->direct_local = 1;
+  d->debug_skip_unit = -1;
+}
+
+const char* ag_matmul_strerror(int code) {
+  switch (code) {
+    case AGMM_OK: return "ok";
+    case AGMM_ERR_INVALID_ARG: return "invalid argument";
+    case AGMM_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case AGMM_ERR_HIP: return "HIP runtime error";
+    case AGMM_ERR_OOM: return "device out of memory";
+    case AGMM_ERR_TIMEOUT: return "flag wait timed out";
+    case AGMM_ERR_WRONG_DEVICE: return "current device differs from the handle's device";
+    case AGMM_ERR_POISONED: return "handle poisoned by an earlier timeout";
+    default: return "unknown error code";
+  }
+}
+
+int ag_matmul_last_hip_error(void) { return g_last_hip; }
+
+int64_t ag_matmul_workspace_bytes(const agmm_desc* desc) {
+  const int rc = validate_desc(desc);
+  if (rc != AGMM_OK) return rc;
+  Plan pl;
+  // The CU count only shapes the grid; take the MI355X's 256 when no device is asked.
+  const int prc = make_plan(*desc, 256, &pl);
+  if (prc != AGMM_OK) return prc;
+  return pl.total;
+}
+
+int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
+  if (!out_handle) return AGMM_ERR_INVALID_ARG;
+  *out_handle = nullptr;
+  int rc = validate_desc(desc);
+  if (rc != AGMM_OK) return rc;
+  int dev = 0;
+  AGMM_HIP(hipGetDevice(&dev));
+  int num_cus = 0;
+  AGMM_HIP(hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+  Plan pl;
+  rc = make_plan(*desc, num_cus, &pl);
+  if (rc != AGMM_OK) return rc;
+  int per_cu = 0;
+  AGMM_HIP(agmm::fused_occupancy(desc->dtype, pl.cfg.block_m, &per_cu));
+  if (per_cu < 1) return AGMM_ERR_UNSUPPORTED;
+
+  agmm_handle* h = new (std::nothrow) agmm_handle();
+  if (!h) return AGMM_ERR_OOM;
+  h->desc = *desc;
+  h->cfg = pl.cfg;
+  h->cfg.device = dev;
+  h->M_s = pl.M_s;
+  h->flags_n = pl.flags_n;
+  h->trace_wgs = pl.trace_wgs;
+  h->h_units = pl.units;
+  h->h_mtiles = pl.mtiles;
+  h->poisoned = false;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)pl.total);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    (void)hipGetLastError();
+    delete h;
+    return e == hipErrorOutOfMemory ? AGMM_ERR_OOM : AGMM_ERR_HIP;
+  }
+  h->staging = reinterpret_cast<uint16_t*>(h->ws + pl.off_staging);
+  h->flags = reinterpret_cast<uint32_t*>(h->ws + pl.off_flags);
+  h->ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_ctr);
+  h->units = reinterpret_cast<uint32_t*>(h->ws + pl.off_units);
+  h->mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_mtiles);
+  h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
+  h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
+
+  auto fail = [&](hipError_t err) {
+    g_last_hip = (int)err;
+    (void)hipFree(h->ws);
+    delete h;
+    return AGMM_ERR_HIP;
+  };
+  // Flags, counters and trace counts start at zero; the schedule tables are uploaded once.
+  if ((e = hipMemset(h->ws + pl.off_flags, 0, (size_t)(pl.off_units - pl.off_flags))) != hipSuccess)
+    return fail(e);
+  if (pl.trace_wgs &&
+      (e = hipMemset(h->ws + pl.off_trace, 0, (size_t)(pl.total - pl.off_trace))) != hipSuccess)
+    return fail(e);
+  if (!pl.units.empty() &&
+      (e = hipMemcpy(h->units, pl.units.data(), pl.units.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail(e);
+  if (!pl.mtiles.empty() &&
+      (e = hipMemcpy(h->mtiles, pl.mtiles.data(), pl.mtiles.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail(e);
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
+  *out_handle = h;
+  return AGMM_OK;
+}
+
+int ag_matmul_destroy(agmm_handle* h) {
+  if (!h) return AGMM_OK;
+  int rc = AGMM_OK;
+  int cur = 0;
+  if (hipGetDevice(&cur) == hipSuccess && cur != h->cfg.device) (void)hipSetDevice(h->cfg.device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipFree(h->ws);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    rc = AGMM_ERR_HIP;
+  }
+  if (cur != h->cfg.device) (void)hipSetDevice(cur);
+  delete h;
+  return rc;
+}
+
+int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg) {
+  if (!h || !cfg) return AGMM_ERR_INVALID_ARG;
+  *cfg = h->cfg;
+  return AGMM_OK;
+}
+
+int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
+                  void* out, void* hip_stream) {
+  if (!h) return AGMM_ERR_INVALID_ARG;
+  if (h->poisoned) return AGMM_ERR_POISONED;
+  const agmm_desc& d = h->desc;
+  const agmm_config& c = h->cfg;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != c.device) return AGMM_ERR_WRONG_DEVICE;
+
+  const int64_t esz = 2;
+  const int64_t shard_bytes = h->M_s * d.K * esz;
+  const int64_t b_bytes = d.K * d.N * esz;
+  const int64_t out_bytes = d.M * d.N * esz;
+  const int64_t bias_bytes = d.has_bias ? d.N * esz : 0;
+  if (!shards) return AGMM_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (d.has_bias != 0)) return AGMM_ERR_INVALID_ARG;
+  for (int i = 0; i < d.D; ++i) {
+    if (shard_bytes > 0 && !shards[i]) return AGMM_ERR_INVALID_ARG;
+    if (misaligned(shards[i])) return AGMM_ERR_INVALID_ARG;
+  }
+  if ((b_bytes > 0 && !B) || misaligned(B)) return AGMM_ERR_INVALID_ARG;
+  if ((out_bytes > 0 && !out) || misaligned(out)) return AGMM_ERR_INVALID_ARG;
+  if (misaligned(bias)) return AGMM_ERR_INVALID_ARG;
+  for (int i = 0; i < d.D; ++i)
+    if (overlaps(out, out_bytes, shards[i], shard_bytes)) return AGMM_ERR_INVALID_ARG;
+  if (overlaps(out, out_bytes, B, b_bytes) || overlaps(out, out_bytes, bias, bias_bytes))
+    return AGMM_ERR_INVALID_ARG;
+  if (c.num_tiles == 0) return AGMM_OK;  // M == 0 or N == 0: nothing to write
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
+    AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
+    h->cfg.epoch = 0;
+  }
+  const uint32_t epoch = ++h->cfg.epoch;
+
+  KParams p;
+  memset(&p, 0, sizeof(p));
+  for (int i = 0; i < d.D; ++i) p.shards[i] = static_cast<const uint16_t*>(shards[i]);
+  p.B = static_cast<const uint16_t*>(B);
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = static_cast<uint16_t*>(out);
+  p.staging = h->staging;
+  p.flags = h->flags;
+  p.ctr = h->ctr;
+  p.units = h->units;
+  p.mtiles = h->mtiles;
+  p.trace = h->trace;
+  p.trace_count = h->trace_count;
+  p.M = d.M;
+  p.N = d.N;
+  p.K = d.K;
+  p.M_s = h->M_s;
+  p.D = d.D;
+  p.rank = d.rank;
+  p.T_m = c.T_m;
+  p.T_n = c.T_n;
+  p.G = c.G;
+  p.kpf = c.k_per_flag;
+  p.num_units = c.num_units;
+  p.num_tiles = c.num_tiles;
+  p.epoch = epoch;
+  p.debug = d.debug;
+  p.trace_cap = c.trace_cap;
+  p.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpinLimit;
+  p.skip_unit = d.debug ? d.debug_skip_unit : -1;
+
+  if (d.algo == AGMM_ALGO_FUSED) {
+    p.F = c.num_fetch_wgs;
+    p.staged_kmajor = d.layout == AGMM_K_CONTIGUOUS ? 1 : 0;
+    AGMM_HIP(agmm::launch_fused(p, d.dtype, c.block_m, c.num_wgs, s));
+  } else {
+    p.F = 0;
+    p.staged_kmajor = 1;  // the baseline gathers into plain [M][K] rows
+    p.debug = 0;
+    p.trace_cap = 0;
+    if (c.num_units > 0) AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
+    const int grid = std::min(c.num_cus, c.num_tiles);
+    AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
+  }
+
+  if (d.debug) {
+    AGMM_HIP(hipStreamSynchronize(s));
+    uint32_t status = 0;
+    AGMM_HIP(hipMemcpy(&status, h->ctr + agmm::CTR_STATUS, 4, hipMemcpyDeviceToHost));
+    if (status != 0) {
+      h->poisoned = true;
+      return AGMM_ERR_TIMEOUT;
+    }
+  }
+  return AGMM_OK;
+}
+
+int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
+  if (!h || !dst) return AGMM_ERR_INVALID_ARG;
+  const agmm_config& c = h->cfg;
+  const void* src = nullptr;
+  size_t n = 0;
+  std::vector<uint32_t> status;
+  switch (what) {
+    case AGMM_Q_FLAGS: src = h->flags; n = (size_t)c.T_m * c.G * 4; break;
+    case AGMM_Q_STAGING: src = h->staging; n = (size_t)c.staging_elems * 2; break;
+    case AGMM_Q_TRACE: src = h->trace; n = (size_t)h->trace_wgs * c.trace_cap * sizeof(agmm_trace_rec); break;
+    case AGMM_Q_TRACE_COUNT: src = h->trace_count; n = (size_t)h->trace_wgs * 4; break;
+    case AGMM_Q_STATUS: src = h->ctr + agmm::CTR_STATUS; n = 16; break;
+    case AGMM_Q_UNITS:
+      if (bytes != h->h_units.size() * 4) return AGMM_ERR_INVALID_ARG;
+      if (bytes) memcpy(dst, h->h_units.data(), bytes);
+      return AGMM_OK;
+    case AGMM_Q_MTILES:
+      if (bytes != h->h_mtiles.size() * 4) return AGMM_ERR_INVALID_ARG;
+      if (bytes) memcpy(dst, h->h_mtiles.data(), bytes);
+      return AGMM_OK;
+    default: return AGMM_ERR_INVALID_ARG;
+  }
+  if (bytes != n) return AGMM_ERR_INVALID_ARG;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != c.device) return AGMM_ERR_WRONG_DEVICE;
+  AGMM_HIP(hipDeviceSynchronize());
+  if (n) AGMM_HIP(hipMemcpy(dst, src, n, hipMemcpyDeviceToHost));
+  return AGMM_OK;
+}
+
+int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {
+  if (!h) return AGMM_ERR_INVALID_ARG;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != h->cfg.device) return AGMM_ERR_WRONG_DEVICE;
+  AGMM_HIP(agmm::launch_fill16(h->staging, h->cfg.staging_elems, pattern,
+                               reinterpret_cast<hipStream_t>(hip_stream)));
+  return AGMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "agmm.h"
+
+namespace agmm {
+
+constexpr int kThreads = 256;  // 4 wave64s per workgroup
+
+// Counter words in the workspace (uint32).
+enum : int {
+  CTR_TILE = 0,         // next output tile to hand out (dynamic tile queue)
+  CTR_DONE = 1,         // workgroups that finished; the last one resets TILE and DONE
+  CTR_STATUS = 2,       // 0 = ok, 1 = a flag wait timed out (sticky until the host clears it)
+  CTR_STATUS_WG = 3,    // workgroup that timed out
+  CTR_STATUS_FLAG = 4,  // flag index it waited on
+  CTR_STATUS_SEEN = 5,  // flag value it last saw
+  CTR_WORDS = 64
+};
+
+// Everything a launch needs, passed by value as the kernel argument.
+struct KParams {
+  const uint16_t* shards[AGMM_MAX_SHARDS];
+  const uint16_t* B;
+  const uint16_t* bias;     // nullptr: no bias
+  uint16_t* out;
+  uint16_t* staging;
+  uint32_t* flags;          // [T_m * G]
+  uint32_t* ctr;            // [CTR_WORDS]
+  const uint32_t* units;    // [2 * num_units]: (m-tile, k-group) in fetch order
+  const uint32_t* mtiles;   // [T_m]: m-tile in GEMM order; bit 31 set = read in place
+  agmm_trace_rec* trace;    // [gridDim.x * trace_cap] (debug)
+  uint32_t* trace_count;    // [gridDim.x] (debug)
+  int64_t M, N, K, M_s;
+  int32_t D, rank, T_m, T_n, G, kpf;
+  int32_t num_units, num_tiles, F;
+  int32_t staged_kmajor;    // 1: staging is [M][K]; 0: staging is [K][M]
+  uint32_t epoch;
+  int32_t debug, trace_cap;
+  uint32_t spin_limit;
+  int32_t skip_unit;
+};
+
+// Launchers (defined in agmm_kernels.hip). block_m selects the tile family.
+hipError_t launch_fused(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
+hipError_t launch_gemm_only(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
+hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s);
+hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
+hipError_t launch_fill32(uint32_t* dst, int64_t n, uint32_t v, hipStream_t s);
+// Resident workgroups per CU for the fused kernel of this family (occupancy query).
+hipError_t fused_occupancy(int dtype, int block_m, int* per_cu);
+
+}  // namespace agmm

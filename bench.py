@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused all-gather + GEMM on one MI355X.
+
+A step is one ag_matmul_run over the resident synthetic inputs of the headline workload
+(16384x3584x8192 fp16, D=8 shards of 2048 rows, fp16 bias, m_contiguous staging, local
+shard read in place). Warmup steps are untimed; the K timed steps are bracketed by device
+synchronizations and timed twice: wall clock over the whole region, and HIP events around
+every launch on the launch stream (the fused path is one kernel per step, so the events
+time that kernel). TFLOP/s counts 2*M*N*K per step with M the full gathered row count, the
+convention of the iris issue's results tables.
+
+Prints ONE JSON line on stdout. `--sweep` additionally writes a table of all five workloads
+(fused, copy-barrier-GEMM baseline, and torch.matmul on pre-gathered A as a yardstick) to
+stderr and, with --out, to a JSON-lines file.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % MFMA peak, fused AG+GEMM 16384x3584x8192 fp16, D=8, 1 GPU"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def tflops(M, N, K, seconds):
+    """2*M*N*K / t in TFLOP/s (the pages' convention, M = gathered rows)."""
+    return 2.0 * M * N * K / seconds / 1e12
+
+
+def time_runs(op, dev, steps, warmup, torch):
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        op.run(dev.shards, dev.B, dev.bias, out=dev.out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(s)
+        op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+        b.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]   # ms
+    return wall, per
+
+
+def bench_workload(w, algo, steps, warmup, torch, A, inputs=None, dev=None, **tun):
+    from workloads import make_inputs
+    inp = inputs if inputs is not None else make_inputs(w)
+    if dev is None:
+        dev = inp.to("cuda")
+        dev.out = torch.empty((w.M, w.N), dtype=w.torch_dtype(), device="cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=algo, rank=w.rank,
+                    direct_local=w.direct_local, has_bias=w.has_bias, **tun)
+    wall, per = time_runs(op, dev, steps, warmup, torch)
+    cfg = op.config.as_dict()
+    op.close()
+    return {"wall_s": wall, "per_ms": per, "config": cfg, "inputs": inp, "dev": dev}
+
+
+def yardstick_matmul(w, dev, steps, warmup, torch):
+    """torch.matmul on a pre-gathered A (library GEMM, context only)."""
+    Ag = torch.cat(dev.shards, 0)
+    for _ in range(warmup):
+        torch.matmul(Ag, dev.B)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.matmul(Ag, dev.B)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def cpu_baseline(w, inp, gpu_out, target_s):
+    """The oracle, as it stands, on a bounded sample of output rows of the same workload."""
+    import numpy as np
+    import oracle
+    from workloads import bits
+    sh = [bits(s) for s in inp.shards]
+    Bb = bits(inp.B)
+    bias = bits(inp.bias) if inp.bias is not None else None
+    thr = oracle.max_threads()
+    rows = max(1, min(w.M, 2 * thr))
+    t0 = time.perf_counter()
+    C, _, used = oracle.agmm(w.dtype, sh, Bb, bias, 0, rows)
+    t = time.perf_counter() - t0
+    if t < target_s / 3 and rows < w.M:
+        rows = int(min(w.M, max(rows + 1, rows * target_s / max(t, 1e-3))))
+        t0 = time.perf_counter()
+        C, _, used = oracle.agmm(w.dtype, sh, Bb, bias, 0, rows)
+        t = time.perf_counter() - t0
+    got = gpu_out[:rows].detach().cpu().contiguous().view(__import__("torch").int16).numpy()
+    chk = oracle.check(w.dtype, got.view(np.uint16), C)
+    return {"value": round(tflops(rows, w.N, w.K, t), 6), "unit": "TFLOP/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": f"output rows 0..{rows - 1} of {w.M} ({rows}x{w.N}x{w.K}), {t:.2f} s, "
+                      f"fp64 C oracle, OpenMP over rows",
+            "parity_rows_bad": int(chk["bad"]), "parity_max_err_over_tol": chk["max_ratio"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ag_16384x3584x8192_d8_f16_bias")
+    ap.add_argument("--algo", default="fused", choices=["fused", "baseline"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the requested algorithm (for profiler runs)")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--fetch-wgs", type=int, default=0)
+    ap.add_argument("--k-per-flag", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the multi-GPU path is a design, not code, here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import all_gather_gemm_amd as A
+    from workloads import BY_NAME, WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    tun = {}
+    if args.block_m:
+        tun["block_m"] = args.block_m
+    if args.fetch_wgs:
+        tun["num_fetch_wgs"] = args.fetch_wgs
+    if args.k_per_flag:
+        tun["k_per_flag"] = args.k_per_flag
+
+    if args.sweep:
+        rows = []
+        for w in WORKLOADS:
+            rf = bench_workload(w, "fused", args.steps, args.warmup, torch, A, **tun)
+            rb = bench_workload(w, "baseline", args.steps, args.warmup, torch, A,
+                                inputs=rf["inputs"], dev=rf["dev"], **tun)
+            ym = yardstick_matmul(w, rf["dev"], args.steps, args.warmup, torch)
+            mf, mb = statistics.median(rf["per_ms"]), statistics.median(rb["per_ms"])
+            row = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "D": w.D,
+                   "dtype": w.dtype, "layout": w.layout,
+                   "fused_ms_median": mf, "fused_ms_min": min(rf["per_ms"]),
+                   "baseline_ms_median": mb, "speedup": mb / mf,
+                   "fused_tflops": tflops(w.M, w.N, w.K, mf / 1e3),
+                   "baseline_tflops": tflops(w.M, w.N, w.K, mb / 1e3),
+                   "pct_peak": 100 * tflops(w.M, w.N, w.K, mf / 1e3) / PEAK_TFLOPS[w.dtype],
+                   "torch_matmul_pregathered_ms": ym, "block_m": rf["config"]["block_m"],
+                   "fetch_wgs": rf["config"]["num_fetch_wgs"], "wgs": rf["config"]["num_wgs"]}
+            rows.append(row)
+            print("| {workload} | {fused_ms_median:.4f} | {baseline_ms_median:.4f} | "
+                  "{speedup:.2f}x | {fused_tflops:.1f} | {pct_peak:.1f}% | "
+                  "{torch_matmul_pregathered_ms:.4f} | {block_m} |".format(**row),
+                  file=sys.stderr, flush=True)
+            del rf, rb
+            torch.cuda.empty_cache()
+        if args.out:
+            with open(args.out, "w") as fh:
+                for r in rows:
+                    fh.write(json.dumps(r) + "\n")
+
+    w = BY_NAME[args.workload]
+    r = bench_workload(w, args.algo, args.steps, args.warmup, torch, A, **tun)
+    per = r["per_ms"]
+    ms_step = r["wall_s"] * 1e3 / args.steps
+    value = tflops(w.M, w.N, w.K, r["wall_s"] / args.steps)
+    avg_ms = sum(per) / len(per)
+    achieved = tflops(w.M, w.N, w.K, avg_ms / 1e3)
+    peak = PEAK_TFLOPS[w.dtype]
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; see workloads.py)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "D": w.D,
+                   "shard_rows": w.M_s, "layout": w.layout, "bias": w.has_bias,
+                   "direct_local": w.direct_local, "rank": w.rank, "algo": args.algo,
+                   "block_m": r["config"]["block_m"], "block_k": r["config"]["block_k"],
+                   "k_per_flag": r["config"]["k_per_flag"],
+                   "fetch_wgs": r["config"]["num_fetch_wgs"], "wgs": r["config"]["num_wgs"]},
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "latency_ms": {"median": round(statistics.median(per), 5), "min": round(min(per), 5),
+                       "p90": round(sorted(per)[int(0.9 * (len(per) - 1))], 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "agmm_persistent (fused)" if args.algo == "fused" else
+                               "agmm_copy + agmm_persistent (gemm only)",
+                     "per_launch_flops": 2.0 * w.M * w.N * w.K,
+                     "avg_launch_ms": round(avg_ms, 5)},
+    }
+    if not args.no_cpu_baseline:   # before the extras reuse the output buffer
+        res["cpu_baseline"] = cpu_baseline(w, r["inputs"], r["dev"].out, args.cpu_seconds)
+    if not args.no_extras:
+        other = "baseline" if args.algo == "fused" else "fused"
+        rb = bench_workload(w, other, args.steps, args.warmup, torch, A, inputs=r["inputs"],
+                            dev=r["dev"], **tun)
+        mb = statistics.median(rb["per_ms"])
+        res[f"{other}_variant"] = {"median_ms": round(mb, 5),
+                                   "tflops": round(tflops(w.M, w.N, w.K, mb / 1e3), 3),
+                                   "fused_speedup": round((mb / statistics.median(per))
+                                                          if other == "baseline" else
+                                                          (statistics.median(per) / mb), 3)}
+        ym = yardstick_matmul(w, r["dev"], args.steps, args.warmup, torch)
+        res["yardstick_torch_matmul_pregathered"] = {
+            "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}
+        # staging traffic of the fused step: 2 * (staged rows) * K * 2 bytes (read + write)
+        staged_bytes = 2 * (w.M - (w.M_s if w.direct_local else 0)) * w.K * 2
+        res["staging"] = {"bytes_per_step": staged_bytes,
+                          "gbs_over_step": round(staged_bytes / (avg_ms / 1e3) / 1e9, 1),
+                          "peak_gbs": PEAK_HBM_GBS}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * agmm.h — fused all-gather + GEMM for AMD MI355X (gfx950): the C ABI.
+ *
+ * Operation (pytorch/helion PR "[Benchmark] Add all gather matmul benchmark", Kraken
+ * optimization comment: a = all_gather(a_shared), out = a @ b; the same comment's
+ * local-tile index formula fixes the row order):
+ *
+ *     out[M, N] = concat(shard_0, ..., shard_{D-1})[M, K] @ B[K, N]  (+ bias[N])
+ *
+ * Shard d is a row-major [M/D, K] matrix holding global rows [d*M/D, (d+1)*M/D). All
+ * matrices are row-major and contiguous; inputs, bias and output share one 16-bit type
+ * (fp16 or bf16); products accumulate in fp32 and the result is rounded once (RNE).
+ *
+ * Method (ROCm/iris issue "Fused all-gather+GEMM HBM-buffer kernel for iris.ops", opening
+ * summary and "New kernel"): one persistent kernel splits its workgroups into fetchers
+ * and GEMM workers. Fetchers copy A tiles into a local HBM staging buffer (k_contiguous
+ * or m_contiguous layout) and publish one ready flag per tile; GEMM workers wait on those
+ * flags and compute each output tile as its A tiles arrive, so there is no whole-gather
+ * barrier. Tiles of the local shard (`rank`) are read in place and never staged (Helion
+ * thread, Kraken optimization). A baseline variant copies every staged tile first, then
+ * runs the GEMM (the barrier-based baseline of the iris issue).
+ *
+ * On one GPU the D shards are D separate device allocations standing in for the D ranks'
+ * shards; the staging copy is the all-gather's local half.
+ *
+ * Threading: a handle is used by one host thread at a time. Errors are returned as
+ * negative codes; no C++ exception or abort crosses this interface.
+ */
+#ifndef AGMM_H
+#define AGMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AGMM_MAX_SHARDS 64
+
+/* ---- return codes ---- */
+#define AGMM_OK 0
+#define AGMM_ERR_INVALID_ARG (-1)  /* null / misaligned pointer, bad count, aliasing output */
+#define AGMM_ERR_UNSUPPORTED (-2)  /* a shape or option this build does not handle */
+#define AGMM_ERR_HIP (-3)          /* a HIP runtime call failed; see ag_matmul_last_hip_error */
+#define AGMM_ERR_OOM (-4)          /* device allocation failed */
+#define AGMM_ERR_TIMEOUT (-5)      /* a flag wait exceeded its spin limit; handle is poisoned */
+#define AGMM_ERR_WRONG_DEVICE (-6) /* current HIP device differs from the handle's device */
+#define AGMM_ERR_POISONED (-7)     /* an earlier run timed out; destroy and recreate */
+
+/* ---- enumerations ---- */
+#define AGMM_F16 0
+#define AGMM_BF16 1
+
+/* Staging-buffer layout (iris issue, "New kernel": k_contiguous and m_contiguous staged-A
+ * layouts, named but not defined there). Reading used here: the unit-stride dimension of
+ * the staging buffer. k_contiguous: staging is [M][K], element (m, k) at m*K + k (a straight
+ * copy of the gathered rows). m_contiguous: staging is [K][M], element (m, k) at k*M + m
+ * (the fetcher transposes). */
+#define AGMM_K_CONTIGUOUS 0
+#define AGMM_M_CONTIGUOUS 1
+
+#define AGMM_ALGO_FUSED 0     /* fetcher + GEMM workgroups in one persistent kernel */
+#define AGMM_ALGO_BASELINE 1  /* copy kernel, then stream order (the barrier), then GEMM */
+
+/* Problem and tuning description. Fields marked "0 = auto" are chosen by create. */
+typedef struct agmm_desc {
+  int32_t D;             /* number of shards, 1..AGMM_MAX_SHARDS */
+  int32_t rank;          /* index of the local shard, 0..D-1 */
+  int64_t M, N, K;       /* gathered rows (M = D * M_shard), columns, inner dimension */
+  int32_t dtype;         /* AGMM_F16 or AGMM_BF16 for shards, B, bias and out */
+  int32_t layout;        /* AGMM_K_CONTIGUOUS or AGMM_M_CONTIGUOUS (fused algorithm) */
+  int32_t algo;          /* AGMM_ALGO_FUSED or AGMM_ALGO_BASELINE */
+  int32_t direct_local;  /* 1: local-shard tiles read in place; 0: every tile staged */
+  int32_t has_bias;      /* 1: run() takes a bias[N] pointer; 0: bias must be NULL */
+  int32_t debug;         /* 1: record per-workgroup trace; run() synchronizes and reports
+                            a flag-wait timeout as AGMM_ERR_TIMEOUT */
+  int32_t block_m;       /* output tile edge: 64, 128 or 256 (tile is square); 0 = auto */
+  int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto (1024 columns) */
+  int32_t num_fetch_wgs; /* fetcher workgroups (fused); 0 = auto */
+  int32_t num_wgs;       /* workgroups in the persistent grid; 0 = one per compute unit */
+  int32_t trace_cap;     /* debug trace records per workgroup; 0 = auto */
+  uint32_t spin_limit;   /* flag polls before a wait gives up; 0 = auto (several seconds) */
+  int32_t debug_skip_unit; /* debug: fetch unit whose flag is never published; -1 = none */
+  int32_t reserved[3];
+} agmm_desc;
+
+/* Configuration resolved by create (read back with ag_matmul_get_config). */
+typedef struct agmm_config {
+  int32_t block_m, block_n, block_k, k_per_flag;
+  int32_t T_m, T_n, G;          /* m-tiles, n-tiles, k-groups (one flag per m-tile x k-group) */
+  int32_t num_units;            /* staged (m-tile, k-group) units */
+  int32_t num_tiles;            /* output tiles */
+  int32_t num_fetch_wgs;        /* F */
+  int32_t num_wgs;              /* W, fused grid (fetchers included) */
+  int32_t num_copy_wgs;         /* baseline copy-kernel grid */
+  int32_t trace_cap;
+  uint32_t epoch;               /* epoch of the last run (0 before the first) */
+  int64_t staging_elems;        /* 16-bit elements in the staging buffer */
+  int64_t workspace_bytes;      /* device bytes the handle owns */
+  int32_t device;               /* HIP device the handle was created on */
+  int32_t num_cus;
+  int32_t reserved[4];
+} agmm_config;
+
+typedef struct agmm_handle agmm_handle;
+
+/* Fills `desc` with defaults: D=1, rank=0, fp16, k_contiguous, fused, direct_local=1, no
+ * bias, no debug, every tunable auto, debug_skip_unit=-1. */
+void ag_matmul_desc_init(agmm_desc* desc);
+
+/*
+ * Creates a handle for one problem shape on the current HIP device: validates `desc`,
+ * chooses the tile configuration, and allocates and zeroes the workspace (staging buffer
+ * of M*K elements, flags[T_m*G] uint32, schedule tables, counters, optional trace). This is
+ * the preamble of the iris issue ("API / config changes": ..._preamble), done once so that
+ * run() allocates nothing.
+ * Returns AGMM_OK and *out_handle, or INVALID_ARG / UNSUPPORTED / OOM / HIP.
+ * Shape rules: M % D == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows); m_contiguous also
+ * needs M % 8 == 0. M, N, K may be zero (run() then only writes what exists: K == 0 gives
+ * out = bias or 0). M, N, K < 2^23 (UNSUPPORTED otherwise).
+ */
+int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
+
+/*
+ * Enqueues one run on `hip_stream` (a hipStream_t; NULL = the null stream) and returns
+ * without synchronizing (except in debug mode).
+ *   shards: host array of D device pointers, shard d = [M/D, K] row-major;
+ *   B:      device [K, N] row-major;  bias: device [N] or NULL (must match has_bias);
+ *   out:    device [M, N] row-major, must not overlap any input.
+ * Every device pointer must be 16-byte aligned. The caller keeps all buffers alive until
+ * the stream work completes. One run may be in flight per handle; successive runs on one
+ * stream are safe; concurrent runs of one handle on different streams are undefined.
+ * Returns AGMM_OK, INVALID_ARG, WRONG_DEVICE, POISONED, HIP, or (debug) TIMEOUT.
+ */
+int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
+                  void* out, void* hip_stream);
+
+/* Synchronizes the handle's device and frees its workspace. NULL-safe. */
+int ag_matmul_destroy(agmm_handle* h);
+
+/* Device bytes create would allocate for `desc` (after resolving auto fields), or a
+ * negative error code. Pure host computation; touches no device. */
+int64_t ag_matmul_workspace_bytes(const agmm_desc* desc);
+
+/* Static text for a return code. */
+const char* ag_matmul_strerror(int code);
+
+/* Last hipError_t seen by this library in the calling thread (0 if none). */
+int ag_matmul_last_hip_error(void);
+
+/* Copies the resolved configuration. */
+int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg);
+
+/* ---- debug / bookkeeping access (synchronizes the handle's device) ---- */
+#define AGMM_Q_FLAGS 1        /* uint32[T_m * G] ready flags */
+#define AGMM_Q_STAGING 2      /* uint16[staging_elems] staging buffer */
+#define AGMM_Q_TRACE 3        /* agmm_trace_rec[num_wgs * trace_cap] */
+#define AGMM_Q_TRACE_COUNT 4  /* uint32[num_wgs] records written per workgroup */
+#define AGMM_Q_STATUS 5       /* uint32[4]: {status, workgroup, flag index, value seen} */
+#define AGMM_Q_UNITS 6        /* uint32[2 * num_units]: (m-tile, k-group) in fetch order */
+#define AGMM_Q_MTILES 7       /* uint32[T_m]: m-tile in GEMM order, bit 31 = read in place */
+
+/* Trace events (debug). One record per fetched unit, per computed tile and per flag wait
+ * of wave 0, after the per-workgroup event ids of the iris issue (wg_fetch, wg_gemm,
+ * wg_gemm_wait). Timestamps are the GPU's constant 100 MHz real-time counter. */
+#define AGMM_EV_FETCH 1      /* id = unit index, a = m-tile, b = k-group */
+#define AGMM_EV_GEMM 2       /* id = tile index, a = m-tile, b = n-tile */
+#define AGMM_EV_GEMM_WAIT 3  /* id = flag index, a = value seen, b = polls */
+
+typedef struct agmm_trace_rec {
+  uint32_t event, id, a, b;
+  uint64_t t0, t1;
+} agmm_trace_rec;
+
+/* Copies `bytes` bytes of the queried buffer into host memory `dst` (bytes must equal the
+ * buffer's size). Synchronizes the device first. */
+int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes);
+
+/* Fills the staging buffer with a 16-bit pattern (a NaN pattern exposes reads of unwritten
+ * staging) on `hip_stream`. */
+int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGMM_H */

@@ -1,0 +1,124 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function include/agmm.h
+declares, and its host-side logic (defaults, validation, workspace sizing, error strings)
+behaves as documented. Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "all_gather_gemm_amd", "libagmm.so")
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not os.path.exists(LIB):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "agmm_build", os.path.join(ROOT, "all_gather_gemm_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import all_gather_gemm_amd
+    return all_gather_gemm_amd
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "agmm.h")) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ag_matmul_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(A):
+    names = header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in agmm.h but not exported"
+    assert set(names) == set(A.EXPORTED)
+
+
+def test_desc_defaults(A):
+    d = A.ag_matmul_desc_init()
+    assert (d.D, d.rank, d.dtype, d.layout, d.algo, d.direct_local, d.has_bias, d.debug) == \
+        (1, 0, A.F16, A.K_CONTIGUOUS, A.ALGO_FUSED, 1, 0, 0)
+    assert d.debug_skip_unit == -1 and d.block_m == 0 and d.spin_limit == 0
+
+
+def test_strerror(A):
+    assert A.strerror(0) == "ok"
+    for code in range(-7, 0):
+        assert A.strerror(code) and A.strerror(code) != "unknown error code"
+    assert A.strerror(-99) == "unknown error code"
+
+
+def _ws(A, **kw):
+    return A.ag_matmul_workspace_bytes(A.ag_matmul_desc_init(**kw))
+
+
+def test_validation_errors(A):
+    INV, UNS = -1, -2
+    assert _ws(A, D=0, M=8, N=8, K=8) == INV
+    assert _ws(A, D=65, M=65 * 8, N=8, K=8) == INV
+    assert _ws(A, D=2, rank=2, M=8, N=8, K=8) == INV
+    assert _ws(A, D=3, M=8, N=8, K=8) == INV            # M % D
+    assert _ws(A, D=1, M=-1, N=8, K=8) == INV
+    assert _ws(A, D=1, M=8, N=12, K=8) == UNS          # N % 8
+    assert _ws(A, D=1, M=8, N=8, K=12) == UNS          # K % 8
+    assert _ws(A, D=2, M=2 * 5, N=8, K=8, layout=A.M_CONTIGUOUS) == UNS  # M % 8
+    assert _ws(A, D=1, M=8, N=8, K=8, block_m=96) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, dtype=2) == INV
+    assert _ws(A, D=1, M=1 << 23, N=8, K=8) == UNS
+    assert _ws(A, D=1, M=8, N=8, K=8, has_bias=2) == INV
+    # create rejects before touching a device
+    with pytest.raises(A.AgmmError) as e:
+        A.ag_matmul_create(A.ag_matmul_desc_init(D=0))
+    assert e.value.code == INV
+    # NULL handles
+    assert A.ag_matmul_destroy(None) == 0
+    assert A.lib.ag_matmul_run(None, None, None, None, None, None) == INV
+
+
+def test_workspace_bytes_large(A):
+    # 16384x3584x8192, D=8, tile 256: staging M*K fp16, flags T_m*G, 56 staged m-tiles x 8
+    # k-groups of 8-byte unit records, 64 m-tile records, counters; 256-byte aligned pieces.
+    al = lambda x: (x + 255) & ~255
+    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al(64 * 4) + al(56 * 8 * 8) + al(64 * 4)
+           + 0 + al(4))
+    got = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1)
+    assert got == exp
+    # direct_local off: all 64 m-tiles staged
+    got2 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, direct_local=0)
+    assert got2 - got == al(64 * 8 * 8) - al(56 * 8 * 8)
+    # D=1 with direct reads: nothing staged, no staging buffer
+    assert _ws(A, D=1, M=1024, N=1024, K=1024, block_m=128) < 1 << 16
+
+
+def test_struct_layout_matches_header(A, tmp_path):
+    """The ctypes mirrors of agmm_desc / agmm_config / agmm_trace_rec have the C layout:
+    compile a probe against include/agmm.h with the host C compiler and compare offsets."""
+    import subprocess
+    structs = {"agmm_desc": A.agmm_desc, "agmm_config": A.agmm_config,
+               "agmm_trace_rec": A.agmm_trace_rec}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "agmm.h"', "int main(void){"]
+    for sname, cls in structs.items():
+        lines.append(f'printf("{sname} size %zu\\n", sizeof({sname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{sname} {f} %zu\\n", offsetof({sname}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line.strip():
+            sname, f, v = line.split()
+            got[(sname, f)] = int(v)
+    for sname, cls in structs.items():
+        assert got[(sname, "size")] == ctypes.sizeof(cls), sname
+        for f, _ in cls._fields_:
+            assert got[(sname, f)] == getattr(cls, f).offset, (sname, f)

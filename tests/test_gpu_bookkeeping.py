@@ -1,0 +1,140 @@
+"""GPU bookkeeping, bit for bit against the schedule model (oracle/schedule_model.py):
+schedule tables, final flag array, staging contents (staging poisoned with NaN first), the
+per-fetcher unit sequence, every output tile computed exactly once, every wait seeing the
+run's epoch. Also: stale-staging races (alternating inputs, poisoned staging), and the
+bounded flag wait (a unit whose flag the host never lets the fetcher publish)."""
+import numpy as np
+import pytest
+
+from agmm_testlib import NAN16, oracle_full, out_bits, run_gpu
+from oracle import schedule_model as sm
+from workloads import Workload, bits, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    Workload("bk_k", 4, 4 * 256, 512, 2048, "f16", "normal_sqrtk", True, "k_contiguous", True, 31,
+             rank=2),
+    Workload("bk_m", 3, 3 * 200, 264, 1096, "bf16", "normal_sqrtk", False, "m_contiguous", True,
+             32, rank=0),
+    Workload("bk_off", 2, 2 * 128, 384, 640, "f16", "uniform", False, "k_contiguous", False, 33,
+             rank=1),
+]
+
+
+def geometry(w, cfg):
+    return sm.Geometry(w.D, w.M, w.N, w.K, cfg["block_m"], cfg["block_n"], cfg["block_k"],
+                       cfg["k_per_flag"], w.rank, w.direct_local, cfg["num_fetch_wgs"],
+                       cfg["num_wgs"])
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("bm", [64, 128])
+def test_bookkeeping_matches_model(w, bm):
+    import torch
+    import all_gather_gemm_amd as A
+    print(f"case {w.name} bm={bm}", flush=True)
+    inp = make_inputs(w)
+    g_in = inp.to("cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
+                    direct_local=w.direct_local, has_bias=w.has_bias, debug=True, block_m=bm,
+                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096)
+    cfg = op.config.as_dict()
+    g = geometry(w, cfg)
+    # tables
+    assert [tuple(u) for u in op.units()] == sm.fetch_units(g)
+    mt = op.mtiles()
+    assert [int(x & 0x7FFFFFFF) for x in mt] == sm.mtile_order(g)
+    assert [bool(x >> 31) for x in mt] == [sm.is_direct(g, t) for t in sm.mtile_order(g)]
+    C, _ = oracle_full(w, inp)
+    A_bits = np.concatenate([bits(s) for s in inp.shards])
+    prior = np.zeros(g.T_m * g.G, dtype=np.uint32)
+    for epoch in (1, 2, 3):
+        op.fill_staging(NAN16[w.dtype])
+        out = op.run(g_in.shards, g_in.B, g_in.bias)
+        torch.cuda.synchronize()
+        import oracle
+        r = oracle.check(w.dtype, out_bits(out), C)
+        assert r["bad"] == 0, r
+        flags = op.flags()
+        exp = sm.expected_flags(g, epoch, prior)
+        assert np.array_equal(flags, exp)
+        prior = flags.copy()
+        if cfg["staging_elems"]:
+            st = op.staging()
+            assert np.array_equal(st, sm.expected_staging(g, A_bits, w.layout, NAN16[w.dtype]))
+        counts, recs = op.trace()
+        assert (counts <= cfg["trace_cap"]).all()
+        fetched = {f: [] for f in range(g.F)}
+        tiles = []
+        for wg in range(cfg["num_wgs"]):
+            for rec in recs[wg, :counts[wg]]:
+                if rec["event"] == A.EV_FETCH:
+                    fetched[wg].append(int(rec["id"]))
+                    assert (int(rec["a"]), int(rec["b"])) == sm.fetch_units(g)[rec["id"]]
+                elif rec["event"] == A.EV_GEMM:
+                    tiles.append(int(rec["id"]))
+                    assert (int(rec["a"]), int(rec["b"])) == sm.gemm_tiles(g)[rec["id"]]
+                elif rec["event"] == A.EV_GEMM_WAIT:
+                    assert int(rec["a"]) == epoch
+                    t_m, kg = divmod(int(rec["id"]), g.G)
+                    assert not sm.is_direct(g, t_m)
+                else:
+                    raise AssertionError(rec)
+            # a workgroup takes tiles in increasing queue order
+            mine = [int(r["id"]) for r in recs[wg, :counts[wg]] if r["event"] == A.EV_GEMM]
+            assert mine == sorted(mine)
+        assert [fetched[f] for f in range(g.F)] == sm.fetcher_lists(g)
+        assert sorted(tiles) == list(range(len(sm.gemm_tiles(g))))
+        assert np.array_equal(op.status(), np.zeros(4, dtype=np.uint32))
+    op.close()
+
+
+def test_alternating_inputs_and_poisoned_staging():
+    """Two input sets alternate while staging is re-poisoned each run: a read of stale or
+    unwritten staging would show up as a mismatch against the baseline output."""
+    import torch
+    w = Workload("alt", 8, 8 * 128, 768, 1536, "f16", "normal_sqrtk", True, "m_contiguous", True,
+                 41, rank=3)
+    sets = [make_inputs(w, seed=s) for s in (41, 42)]
+    dev = [s.to("cuda") for s in sets]
+    refs = [out_bits(run_gpu(w, s, "baseline", dev_inp=d, block_m=128).out)
+            for s, d in zip(sets, dev)]
+    assert not np.array_equal(refs[0], refs[1])
+    import all_gather_gemm_amd as A
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
+                    has_bias=True, block_m=128, k_per_flag=1)
+    for it in range(12):
+        i = it % 2
+        if it % 3 == 0:
+            op.fill_staging(NAN16[w.dtype])
+        out = op.run(dev[i].shards, dev[i].B, dev[i].bias)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), refs[i]), it
+    op.close()
+
+
+def test_flag_wait_is_bounded():
+    """A unit whose flag is never published (set from the host): the waiting workgroup gives
+    up after its spin limit, the run reports a timeout, every workgroup exits, and the
+    handle refuses further runs."""
+    import torch
+    import all_gather_gemm_amd as A
+    w = Workload("skip", 2, 2 * 128, 256, 512, "f16", "uniform", False, "k_contiguous", True, 51)
+    inp = make_inputs(w).to("cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, debug=True, block_m=64, k_per_flag=1,
+                    debug_skip_unit=1, spin_limit=2000)
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    rc = A.ag_matmul_run(op.handle, [s.data_ptr() for s in inp.shards], inp.B.data_ptr(), None,
+                         out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == -5  # TIMEOUT
+    st = op.status()
+    assert st[0] == 1
+    u = op.units()[1]
+    assert st[2] == u[0] * op.config.G + u[1]      # the flag of the skipped unit
+    assert st[3] != 1                               # the run's epoch was 1
+    rc2 = A.ag_matmul_run(op.handle, [s.data_ptr() for s in inp.shards], inp.B.data_ptr(), None,
+                          out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc2 == -7  # POISONED
+    torch.cuda.synchronize()
+    op.close()

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Tolerance (unrounded fp64 reference C): |out - C| <= 2^-7 |C| + 1e-2 for bf16 output and
+2^-10 |C| + 1e-3 for fp16 output. Exact-integer inputs make every fp32 partial sum exact,
+so there the GPU must equal the oracle's rounded result bit for bit. Variants that only
+change where A is read from (fused vs baseline, staging layout, local shard in place or
+staged, shard count D, rank) share one K order on the GPU and must agree bit for bit.
+"""
+import numpy as np
+import pytest
+
+from agmm_testlib import (NAN16, assert_close, oracle_full, oracle_sampled, out_bits, run_gpu,
+                          sample_points)
+from workloads import (LARGE_16384, MID_4096, SQUARE_1024, SQUARE_4096, TINY, Workload,
+                       make_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(w, inp, **kw):
+    f = run_gpu(w, inp, "fused", **kw)
+    b = run_gpu(w, inp, "baseline", **kw)
+    return out_bits(f.out), out_bits(b.out), f.config
+
+
+@pytest.mark.parametrize("w", [TINY, SQUARE_1024], ids=lambda w: w.name)
+def test_small_workloads_full_oracle(w):
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    C, _ = oracle_full(w, inp)
+    fo, bo, cfg = _both(w, inp)
+    assert_close(w, fo, C, "fused")
+    assert_close(w, bo, C, "baseline")
+    assert np.array_equal(fo, bo)
+
+
+RAGGED = [
+    # (D, M_s, N, K, dtype, layout, bias, block_m)
+    (3, 200, 328, 424, "f16", "k_contiguous", True, 64),
+    (3, 200, 328, 424, "bf16", "m_contiguous", False, 64),
+    (2, 136, 264, 1032, "f16", "m_contiguous", True, 128),
+    (4, 72, 520, 200, "bf16", "k_contiguous", True, 128),
+    (2, 264, 392, 1096, "f16", "k_contiguous", False, 256),
+    (5, 104, 264, 136, "f16", "m_contiguous", True, 256),
+    (1, 296, 136, 72, "bf16", "k_contiguous", True, 256),
+]
+
+
+@pytest.mark.parametrize("D,Ms,N,K,dt,layout,bias,bm", RAGGED)
+def test_ragged_shapes_full_oracle(D, Ms, N, K, dt, layout, bias, bm):
+    w = Workload(f"ragged_{D}x{Ms}_{N}_{K}_{dt}_{layout}_{bm}", D, D * Ms, N, K, dt,
+                 "normal_sqrtk", bias, layout, True, 100 + D + K, rank=D - 1)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    C, _ = oracle_full(w, inp)
+    fo, bo, cfg = _both(w, inp, block_m=bm, k_per_flag=1, num_fetch_wgs=3)
+    assert cfg["block_m"] == bm
+    assert_close(w, fo, C, "fused")
+    assert_close(w, bo, C, "baseline")
+    assert np.array_equal(fo, bo)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["k_contiguous", "m_contiguous"])
+@pytest.mark.parametrize("bm", [64, 128, 256])
+def test_exact_integer_bit_exact(dt, layout, bm):
+    w = Workload(f"int_{dt}_{layout}_{bm}", 4, 4 * 192, 520, 776, dt, "int", True, layout, True,
+                 7, rank=1)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    _, out16 = oracle_full(w, inp)
+    fo, bo, _ = _both(w, inp, block_m=bm)
+    assert np.array_equal(fo, out16)
+    assert np.array_equal(bo, out16)
+
+
+def test_k_zero_gives_bias_or_zero():
+    import torch
+    for bias in (False, True):
+        w = Workload(f"k0_{bias}", 2, 64, 72, 0, "f16", "uniform", bias, "k_contiguous", True, 3)
+        inp = make_inputs(w)
+        C, out16 = oracle_full(w, inp)
+        fo, bo, _ = _both(w, inp)
+        assert np.array_equal(fo, out16) and np.array_equal(bo, out16)
+
+
+def test_empty_m_or_n_is_a_noop():
+    import torch
+    import all_gather_gemm_amd as A
+    for (M, N) in ((0, 64), (64, 0)):
+        op = A.AgMatmul(2, M, N, 64)
+        sh = [torch.zeros((M // 2, 64), dtype=torch.float16, device="cuda") for _ in range(2)]
+        B = torch.zeros((64, N), dtype=torch.float16, device="cuda")
+        out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        op.run(sh, B, out=out)
+        torch.cuda.synchronize()
+        op.close()
+
+
+def test_invariances_bit_exact():
+    """Same A cut into D = 1, 2, 4, 8 shards, every rank, both layouts, local shard in place
+    or staged, fused or baseline: one output, bit for bit (one tile configuration)."""
+    base = Workload("inv", 1, 1024, 512, 1536, "bf16", "normal_sqrtk", True, "k_contiguous",
+                    True, 9)
+    inp1 = make_inputs(base)
+    A_full = inp1.shards[0]
+    ref = None
+    for D in (1, 2, 4, 8):
+        ms = base.M // D
+        for rank in sorted({0, D - 1, D // 2}):
+            for layout in ("k_contiguous", "m_contiguous"):
+                for dl in (True, False):
+                    w = base.with_(D=D, rank=rank, layout=layout, direct_local=dl)
+                    inp = type(inp1)([A_full[d * ms:(d + 1) * ms].clone() for d in range(D)],
+                                     inp1.B, inp1.bias)
+                    for algo in ("fused", "baseline"):
+                        o = out_bits(run_gpu(w, inp, algo, block_m=128).out)
+                        if ref is None:
+                            ref = o
+                            C, _ = oracle_full(base, inp1)
+                            assert_close(base, ref, C)
+                        assert np.array_equal(o, ref), (D, rank, layout, dl, algo)
+
+
+@pytest.mark.parametrize("w", [MID_4096, LARGE_16384, SQUARE_4096], ids=lambda w: w.name)
+def test_full_size_sampled_oracle(w):
+    """The headline shapes in the launch configuration the bench times (auto tile config):
+    sampled outputs against the oracle, and fused == baseline over the whole output."""
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    dev = inp.to("cuda")
+    f = run_gpu(w, inp, "fused", dev_inp=dev)
+    b = run_gpu(w, inp, "baseline", dev_inp=dev)
+    fo = out_bits(f.out)
+    rows, cols = sample_points(w, 3000, seed=w.seed, tile=f.config["block_m"])
+    C = oracle_sampled(w, inp, rows, cols)
+    assert_close(w, fo[rows, cols], C, "fused sampled")
+    assert np.array_equal(fo, out_bits(b.out))
+    import oracle
+    assert not np.isnan(oracle.decode(w.dtype, fo)).any()
+
+
+@pytest.mark.parametrize("w", [LARGE_16384, SQUARE_4096], ids=lambda w: w.name)
+def test_full_size_exact_integer_sampled(w):
+    """Full-size shapes with exact-integer inputs: sampled outputs bit-exact."""
+    wi = w.with_(dist="int", name=w.name + "_int")
+    print(f"case {wi.name}", flush=True)
+    inp = make_inputs(wi)
+    f = run_gpu(wi, inp, "fused")
+    fo = out_bits(f.out)
+    rows, cols = sample_points(wi, 2000, seed=5, tile=f.config["block_m"])
+    C = oracle_sampled(wi, inp, rows, cols)
+    import oracle
+    assert np.array_equal(fo[rows, cols], oracle.encode_rne(wi.dtype, C))
