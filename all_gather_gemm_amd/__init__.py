@@ -29,7 +29,7 @@ ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "OOM", -5: "TIMEO
 F16, BF16 = 0, 1
 K_CONTIGUOUS, M_CONTIGUOUS = 0, 1
 ALGO_FUSED, ALGO_BASELINE = 0, 1
-Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES = 1, 2, 3, 4, 5, 6, 7
+Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES, Q_QUEUES = range(1, 9)
 EV_FETCH, EV_GEMM, EV_GEMM_WAIT = 1, 2, 3
 
 EXPORTED = [
@@ -250,6 +250,13 @@ class AgMatmul:
     def mtiles(self) -> np.ndarray:
         n = self.config.T_m
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_MTILES, n * 4), dtype="<u4")
+
+    def queues(self):
+        """[(queue tile ids)] for the 8 per-XCD tile queues."""
+        n = self.config.num_tiles
+        raw = np.frombuffer(ag_matmul_debug_query(self.handle, Q_QUEUES, (16 + n) * 4), dtype="<u4")
+        off, ln, tiles = raw[:8], raw[8:16], raw[16:]
+        return [list(map(int, tiles[o:o + l])) for o, l in zip(off, ln)]
 
     def status(self) -> np.ndarray:
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STATUS, 16), dtype="<u4")

@@ -25,7 +25,9 @@ struct agmm_handle {
   uint32_t* trace_count;
   int64_t flags_n;
   int64_t trace_wgs;        // workgroups the trace buffer has room for
-  std::vector<uint32_t> h_units, h_mtiles;
+  uint32_t* qtiles;
+  std::vector<uint32_t> h_units, h_mtiles, h_qtiles;
+  int32_t qoff[agmm::kQueues], qlen[agmm::kQueues];
   bool poisoned;
 };
 
@@ -85,10 +87,37 @@ bool is_direct(const agmm_desc& d, int64_t M_s, int bm, int64_t t) {
 struct Plan {
   agmm_config cfg;
   int64_t M_s;
-  std::vector<uint32_t> units, mtiles;
+  std::vector<uint32_t> units, mtiles, qtiles;
+  int32_t qoff[agmm::kQueues], qlen[agmm::kQueues];
   int64_t flags_n, trace_wgs;
-  int64_t off_staging, off_flags, off_ctr, off_units, off_mtiles, off_trace, off_tcount, total;
+  int64_t off_staging, off_flags, off_ctr, off_units, off_mtiles, off_qtiles, off_trace,
+      off_tcount, total;
 };
+
+// Tile queues (one per XCD): GEMM-order m-tiles are taken in super-rows of kSuperRows; a
+// super-row's tiles are listed in column blocks of kColBlock n-tiles (so the 32 CUs of an
+// XCD share 4 A row-blocks and 8 B column-blocks in L2), and super-rows are dealt to the
+// queues round-robin. Tile id q = (position of its m-tile in GEMM order) * T_n + n-tile.
+constexpr int kSuperRows = 4;
+constexpr int kColBlock = 8;
+
+void make_queues(int64_t T_m, int64_t T_n, Plan* pl) {
+  std::vector<std::vector<uint32_t>> qs(agmm::kQueues);
+  for (int64_t s0 = 0, j = 0; s0 < T_m; s0 += kSuperRows, ++j) {
+    const int64_t s1 = std::min(T_m, s0 + kSuperRows);
+    auto& q = qs[j % agmm::kQueues];
+    for (int64_t nb = 0; nb < T_n; nb += kColBlock)
+      for (int64_t pos = s0; pos < s1; ++pos)
+        for (int64_t n = nb; n < std::min(T_n, nb + kColBlock); ++n)
+          q.push_back((uint32_t)(pos * T_n + n));
+  }
+  pl->qtiles.clear();
+  for (int x = 0; x < agmm::kQueues; ++x) {
+    pl->qoff[x] = (int32_t)pl->qtiles.size();
+    pl->qlen[x] = (int32_t)qs[x].size();
+    pl->qtiles.insert(pl->qtiles.end(), qs[x].begin(), qs[x].end());
+  }
+}
 
 int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   agmm_config& c = pl->cfg;
@@ -163,6 +192,8 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
       }
   }
 
+  make_queues(T_m, T_n, pl);
+
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
   pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
   c.staging_elems = n_units > 0 ? d.M * d.K : 0;
@@ -174,6 +205,7 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   pl->off_ctr = off;     off = align256(off + agmm::CTR_WORDS * 4);
   pl->off_units = off;   off = align256(off + std::max<int64_t>(1, n_units) * 8);
   pl->off_mtiles = off;  off = align256(off + std::max<int64_t>(1, T_m) * 4);
+  pl->off_qtiles = off;  off = align256(off + std::max<int64_t>(1, T_m * T_n) * 4);
   pl->off_trace = off;   off = align256(off + pl->trace_wgs * c.trace_cap * (int64_t)sizeof(agmm_trace_rec));
   pl->off_tcount = off;  off = align256(off + std::max<int64_t>(1, pl->trace_wgs) * 4);
   pl->total = off;
@@ -256,6 +288,9 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   h->trace_wgs = pl.trace_wgs;
   h->h_units = pl.units;
   h->h_mtiles = pl.mtiles;
+  h->h_qtiles = pl.qtiles;
+  memcpy(h->qoff, pl.qoff, sizeof(h->qoff));
+  memcpy(h->qlen, pl.qlen, sizeof(h->qlen));
   h->poisoned = false;
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)pl.total);
   if (e != hipSuccess) {
@@ -269,6 +304,7 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   h->ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_ctr);
   h->units = reinterpret_cast<uint32_t*>(h->ws + pl.off_units);
   h->mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_mtiles);
+  h->qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_qtiles);
   h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
   h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
 
@@ -289,6 +325,9 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
     return fail(e);
   if (!pl.mtiles.empty() &&
       (e = hipMemcpy(h->mtiles, pl.mtiles.data(), pl.mtiles.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail(e);
+  if (!pl.qtiles.empty() &&
+      (e = hipMemcpy(h->qtiles, pl.qtiles.data(), pl.qtiles.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
   if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
   *out_handle = h;
@@ -365,6 +404,11 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   p.ctr = h->ctr;
   p.units = h->units;
   p.mtiles = h->mtiles;
+  p.qtiles = h->qtiles;
+  for (int x = 0; x < agmm::kQueues; ++x) {
+    p.qoff[x] = h->qoff[x];
+    p.qlen[x] = h->qlen[x];
+  }
   p.trace = h->trace;
   p.trace_count = h->trace_count;
   p.M = d.M;
@@ -431,6 +475,17 @@ int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
       if (bytes != h->h_mtiles.size() * 4) return AGMM_ERR_INVALID_ARG;
       if (bytes) memcpy(dst, h->h_mtiles.data(), bytes);
       return AGMM_OK;
+    case AGMM_Q_QUEUES: {
+      const size_t n = (2 * agmm::kQueues + h->h_qtiles.size()) * 4;
+      if (bytes != n) return AGMM_ERR_INVALID_ARG;
+      uint32_t* o = static_cast<uint32_t*>(dst);
+      for (int x = 0; x < agmm::kQueues; ++x) {
+        o[x] = (uint32_t)h->qoff[x];
+        o[agmm::kQueues + x] = (uint32_t)h->qlen[x];
+      }
+      if (!h->h_qtiles.empty()) memcpy(o + 2 * agmm::kQueues, h->h_qtiles.data(), h->h_qtiles.size() * 4);
+      return AGMM_OK;
+    }
     default: return AGMM_ERR_INVALID_ARG;
   }
   if (bytes != n) return AGMM_ERR_INVALID_ARG;

@@ -10,15 +10,21 @@ namespace agmm {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 
-// Counter words in the workspace (uint32).
+// Output tiles are handed out from kQueues queues, one per XCD (workgroup w is placed on
+// XCD w % 8 by the dispatcher); a workgroup drains its own queue, then steals from the
+// others.
+constexpr int kQueues = 8;
+
+// Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
 enum : int {
-  CTR_TILE = 0,         // next output tile to hand out (dynamic tile queue)
-  CTR_DONE = 1,         // workgroups that finished; the last one resets TILE and DONE
+  CTR_DONE = 0,         // workgroups that finished; the last one resets the queue counters
   CTR_STATUS = 2,       // 0 = ok, 1 = a flag wait timed out (sticky until the host clears it)
   CTR_STATUS_WG = 3,    // workgroup that timed out
   CTR_STATUS_FLAG = 4,  // flag index it waited on
   CTR_STATUS_SEEN = 5,  // flag value it last saw
-  CTR_WORDS = 64
+  CTR_Q = 32,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
+  CTR_QSTRIDE = 32,
+  CTR_WORDS = CTR_Q + kQueues * CTR_QSTRIDE
 };
 
 // Everything a launch needs, passed by value as the kernel argument.
@@ -32,6 +38,8 @@ struct KParams {
   uint32_t* ctr;            // [CTR_WORDS]
   const uint32_t* units;    // [2 * num_units]: (m-tile, k-group) in fetch order
   const uint32_t* mtiles;   // [T_m]: m-tile in GEMM order; bit 31 set = read in place
+  const uint32_t* qtiles;   // [num_tiles]: tile ids, queue by queue
+  int32_t qoff[kQueues], qlen[kQueues];
   agmm_trace_rec* trace;    // [gridDim.x * trace_cap] (debug)
   uint32_t* trace_count;    // [gridDim.x] (debug)
   int64_t M, N, K, M_s;

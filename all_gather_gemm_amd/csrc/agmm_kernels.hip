@@ -68,31 +68,44 @@ struct Num<AGMM_BF16> {
   }
 };
 
-// Tile family: square BMxBM output tile, BK = 16384/BM so that each operand's stage is
-// 2048 chunks (32 KiB): 8 K-major chunks or one 8x8 MN-major block per thread.
+// Tile family: square BMxBM output tile, BK = 16384/BM so that each operand's stage holds
+// 2048 16-byte chunks: 8 K-major chunks or one 8x8 MN-major block per thread.
+//
+// LDS layout of an operand stage: chunk (row r, K-chunk kc) -- 8 consecutive K values of
+// row r -- sits at kc * RS + phys(r), with the chunk-row stride RS = MN + 8 (8 chunks of
+// padding) and phys(r) = r ^ ((r>>3 ^ r>>6) & 7). The padding makes the K-chunk term
+// additive (each MFMA sub-step reads at a fixed offset from one base per lane); the XOR
+// spreads 8x8 transposed blocks. Checked exhaustively: MFMA operand reads, K-major stores
+// (8 rows x 8 K-chunks per wave instruction) and MN-major stores (16 blocks) hit distinct
+// 16-byte bank groups whether a 128-bit LDS access is served 8 or 16 lanes at a time.
 template <int BM_>
 struct Tile {
   static constexpr int BM = BM_, BN = BM_, BK = 16384 / BM_;
   static constexpr int KC = BK / 8;            // 16-byte K-chunks per row
-  static constexpr int A_CH = KC * BM;         // chunks per stage, A
-  static constexpr int B_CH = KC * BN;         // chunks per stage, B
-  static constexpr int STAGE = A_CH + B_CH;    // 4096 chunks = 64 KiB
+  static constexpr int RSA = BM + 8, RSB = BN + 8;
+  static constexpr int A_CH = KC * RSA;        // chunks per stage, A
+  static constexpr int B_CH = KC * RSB;        // chunks per stage, B
+  static constexpr int STAGE = A_CH + B_CH;
   static constexpr int WTM = BM / 2, WTN = BN / 2;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int KSH = (BK == 64) ? 1 : 0;
-  static_assert(A_CH == 2048 && B_CH == 2048, "stage layout");
+  static_assert(2 * STAGE * 16 >= BM * BN * 2, "epilogue tile fits in the stages");
 };
 
-// Physical row of chunk (row r, K-chunk kc) inside a [KC][MN] chunk array. The XOR stays
-// inside r's aligned group of 16 rows, so 16 consecutive rows at one kc (an MFMA operand
-// read by 16 lanes) hit 16 distinct 16-byte bank groups, and so do the 16 lanes of a
-// K-major store (2 rows x 8 kc, or 1 row x 16 kc) and of an MN-major store (16 8x8 blocks).
-template <class T>
-__device__ inline int swz(int r, int kc) {
-  return r ^ (((kc << T::KSH) ^ (r >> 4)) & 15);
-}
+__device__ inline int phys(int r) { return r ^ (((r >> 3) ^ (r >> 6)) & 7); }
 
 __device__ inline u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Row i of the transpose of an 8x8 block of 16-bit values held as 8 rows v[0..7] of four
+// dwords: element j of the result is element i of v[j]. v_perm_b32 picks two 16-bit halves
+// from two dwords per instruction (selector 0x05040100: low halves, 0x07060302: high).
+__device__ inline u32x4 transpose_row(const u32x4 (&v)[8], int i) {
+  const int w = i >> 1;
+  const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(v[2 * q + 1][w], v[2 * q][w], sel);
+  return o;
+}
 __device__ inline void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Buffer resource over [base, base + bytes): loads at byte offsets at or past `bytes`
@@ -108,39 +121,38 @@ __device__ inline u32x4 bload(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-// K-contiguous operand tile (MN rows x BK), element (r, k) at base[r*ld + k]. Offsets are
-// fixed per thread for the whole tile; the resource base moves along K.
+// K-contiguous operand tile (MN rows x BK), element (r, k) at base[r*ld + k]. Chunk
+// c = i*256 + tid is row (c / (8*KC))*8 + c % 8, K-chunk (c / 8) % KC: a wave instruction
+// covers 8 rows x 8 K-chunks (whole 128-byte row segments). A thread's K-chunk is the same
+// for every i and its row advances by 256/KC per i, so its byte offset is off0 + i*rstride.
 template <class T, int MN>
 struct KMajor {
   static constexpr int PER = MN * T::KC / kThreads;
-  u32x4 v[PER];
-  uint32_t off[PER];
+  static constexpr int RPI = kThreads / T::KC;  // rows per i
+  typedef u32x4 Regs[PER];
+  uint32_t off0, rstride;
+  __device__ static inline int row0(int tid) { return (tid / (8 * T::KC)) * 8 + tid % 8; }
+  __device__ static inline int kchunk(int tid) { return (tid / 8) % T::KC; }
   __device__ inline void init(int64_t ld, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = i * kThreads + tid, r = c / T::KC, kc = c % T::KC;
-      off[i] = (uint32_t)((r * ld + kc * 8) * 2);
-    }
+    off0 = (uint32_t)((row0(tid) * ld + kchunk(tid) * 8) * 2);
+    rstride = (uint32_t)(RPI * ld * 2);
   }
   // rs covers the operand from column k0 onwards; k_rem = K - k0. Columns at or past K
   // would read the next row, so the last K-tile of a ragged K is masked explicitly.
-  __device__ inline void load(rsrc_t rs, int64_t k_rem, int tid) {
+  __device__ inline void load(rsrc_t rs, int64_t k_rem, int tid, Regs& v) const {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = bload(rs, off[i]);
-    if (k_rem < T::BK) {
+    for (int i = 0; i < PER; ++i) v[i] = bload(rs, off0 + i * rstride);
+    if (k_rem < T::BK && kchunk(tid) * 8 >= k_rem) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int kc = (i * kThreads + tid) % T::KC;
-        if (kc * 8 >= k_rem) v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int i = 0; i < PER; ++i) v[i] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __device__ inline void store(u32x4* region, int tid) const {
+  __device__ inline void store(u32x4* region, int tid, const Regs& v) const {
+    constexpr int RS = MN + 8;
+    u32x4* base = region + kchunk(tid) * RS;
+    const int r0 = row0(tid);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = i * kThreads + tid, r = c / T::KC, kc = c % T::KC;
-      region[kc * MN + swz<T>(r, kc)] = v[i];
-    }
+    for (int i = 0; i < PER; ++i) base[phys(r0 + i * RPI)] = v[i];
   }
 };
 
@@ -152,28 +164,23 @@ template <class T, int MN>
 struct MNMajor {
   static constexpr int NBM = MN / 8;
   static_assert(NBM * T::KC == kThreads, "one 8x8 block per thread");
-  u32x4 v[8];
+  typedef u32x4 Regs[8];
   uint32_t off0, ld2;
   __device__ inline void init(int64_t ld, int tid) {
     const int nb = tid % NBM, kb = tid / NBM;
     ld2 = (uint32_t)(ld * 2);
     off0 = (uint32_t)((kb * 8 * ld + nb * 8) * 2);
   }
-  __device__ inline void load(rsrc_t rs, int64_t /*k_rem*/, int /*tid*/) {
+  __device__ inline void load(rsrc_t rs, int64_t /*k_rem*/, int /*tid*/, Regs& v) const {
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = bload(rs, off0 + j * ld2);
   }
-  __device__ inline void store(u32x4* region, int tid) const {
+  __device__ inline void store(u32x4* region, int tid, const Regs& v) const {
+    constexpr int RS = MN + 8;
     const int nb = tid % NBM, kb = tid / NBM;
+    u32x4* base = region + kb * RS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1, sh = (i & 1) * 16;
-      u32x4 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        o[p] = ((v[2 * p][w] >> sh) & 0xffffu) | (((v[2 * p + 1][w] >> sh) & 0xffffu) << 16);
-      region[kb * MN + swz<T>(nb * 8 + i, kb)] = o;
-    }
+    for (int i = 0; i < 8; ++i) base[phys(nb * 8 + i)] = transpose_row(v, i);
   }
 };
 
@@ -233,35 +240,43 @@ __device__ inline void wait_flag(const KParams& p, int64_t idx, Tracer& tr) {
   tr.rec(AGMM_EV_GEMM_WAIT, (uint32_t)idx, v, polls, t0);
 }
 
+// MFMA operand fragments of sub-step kk (16 K values): lane l holds row (l % 32) of each
+// 32-row block, K values 8*(l / 32) .. +7.
+template <class T>
+__device__ inline void read_frags(const u32x4* As, const u32x4* Bs, int kk, u32x4 (&a)[T::FM],
+                                  u32x4 (&b)[T::FN], int lane, int wm, int wn) {
+  // lane-dependent part (K-chunk parity and row), then the sub-step as a constant offset
+  const u32x4* pa = As + (lane >> 5) * T::RSA + 2 * kk * T::RSA;
+  const u32x4* pb = Bs + (lane >> 5) * T::RSB + 2 * kk * T::RSB;
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm) a[fm] = pa[phys(wm * T::WTM + fm * 32 + (lane & 31))];
+#pragma unroll
+  for (int fn = 0; fn < T::FN; ++fn) b[fn] = pb[phys(wn * T::WTN + fn * 32 + (lane & 31))];
+}
+
+// B is the MFMA's first operand, so each lane ends up holding 4 consecutive columns of one
+// output row (8-byte stores in the epilogue).
 template <class T, int DT>
-__device__ inline void mma_stage(const u32x4* As, const u32x4* Bs, f32x16 (&acc)[T::FM][T::FN],
-                                 int lane, int wm, int wn) {
+__device__ inline void mfmas(f32x16 (&acc)[T::FM][T::FN], const u32x4 (&a)[T::FM],
+                             const u32x4 (&b)[T::FN]) {
 #pragma unroll
-  for (int kk = 0; kk < T::BK / 16; ++kk) {
-    const int kc = 2 * kk + (lane >> 5);
-    u32x4 a[T::FM], b[T::FN];
+  for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm)
-      a[fm] = As[kc * T::BM + swz<T>(wm * T::WTM + fm * 32 + (lane & 31), kc)];
-#pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn)
-      b[fn] = Bs[kc * T::BN + swz<T>(wn * T::WTN + fn * 32 + (lane & 31), kc)];
-    // B is the MFMA's first operand, so each lane ends up holding 4 consecutive columns
-    // of one output row (8-byte stores in the epilogue).
-#pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = Num<DT>::mfma(b[fn], a[fm], acc[fm][fn]);
-  }
+    for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = Num<DT>::mfma(b[fn], a[fm], acc[fm][fn]);
 }
 
 // One output tile. A_KMAJOR: the A source is K-contiguous (local shard or k_contiguous
 // staging); otherwise it is the m_contiguous staging buffer. WAIT: fused mode, staged
-// k-groups are waited for.
+// k-groups are waited for before their first K-tile is loaded.
+//
+// Pipeline (K-tile t): at the top of step t the global loads of K-tile t+1 are issued into
+// registers; K-tile t is multiplied out of LDS stage t & 1 with the fragments of sub-step
+// kk+1 read while sub-step kk's MFMAs run; during the last sub-step the registers are
+// written (transposed where needed) into the other stage. One barrier per K-tile.
 template <class T, int DT, bool A_KMAJOR, bool WAIT>
-__device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4* lds, int tid,
-                          Tracer& tr) {
-  constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
+__device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4* lds,
+                          u32x2* bias_lds, int tid, Tracer& tr) {
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NKK = BK / 16;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN;
   const int rows_valid = (int)min((int64_t)BM, p.M - m0);
@@ -296,74 +311,112 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
 
   using ALoad = typename std::conditional<A_KMAJOR, KMajor<T, BM>, MNMajor<T, BM>>::type;
+  using BLoad = MNMajor<T, BN>;
   ALoad al;
-  MNMajor<T, BN> bl;
+  BLoad bl;
   al.init(lda, tid);
   bl.init(p.N, tid);
+  typename ALoad::Regs ga;
+  typename BLoad::Regs gb;
+  u32x4 fa[2][T::FM], fb[2][T::FN];
+
   const int KT = (int)((p.K + BK - 1) / BK);
   const int64_t fbase = (int64_t)t_m * p.G;
+  const bool waits = WAIT && staged;
+
+  // This tile's bias slice to LDS (read after the K loop's barriers).
+  if (p.bias && tid < BN / 4)
+    bias_lds[tid] = (n0 + tid * 4 < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n0 + tid * 4)
+                                         : u32x2{0u, 0u};
+
+  // Issue the global loads of K-tile t, after its k-group's flag.
+  auto issue = [&](int t) {
+    if (waits && t % p.kpf == 0) wait_flag(p, fbase + t / p.kpf, tr);
+    const int64_t ka = t * a_step, kb = t * b_step;
+    al.load(make_rsrc(abase + ka, a_bytes - ka * 2), p.K - (int64_t)t * BK, tid, ga);
+    bl.load(make_rsrc(bbase + kb, b_bytes - kb * 2), 0, tid, gb);
+  };
+
   if (KT > 0) {
-    if (WAIT && staged) wait_flag(p, fbase, tr);
-    al.load(make_rsrc(abase, a_bytes), p.K, tid);
-    bl.load(make_rsrc(bbase, b_bytes), p.K, tid);
-    al.store(lds, tid);
-    bl.store(lds + T::A_CH, tid);
+    issue(0);
+    al.store(lds, tid, ga);
+    bl.store(lds + T::A_CH, tid, gb);
     __syncthreads();
-    int next_flag_kt = p.kpf;  // first K-tile of the next k-group
+    read_frags<T>(lds, lds + T::A_CH, 0, fa[0], fb[0], lane, wm, wn);
     for (int kt = 0; kt < KT; ++kt) {
       const int cur = kt & 1;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        if (WAIT && staged && kt + 1 == next_flag_kt) {
-          wait_flag(p, fbase + (kt + 1) / p.kpf, tr);
-          next_flag_kt += p.kpf;
+      const u32x4* As = lds + cur * T::STAGE;
+      const u32x4* Bs = As + T::A_CH;
+      u32x4* An = lds + (cur ^ 1) * T::STAGE;
+      u32x4* Bn = An + T::A_CH;
+      const bool has1 = kt + 1 < KT;
+      if (has1) issue(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK)
+          read_frags<T>(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], lane, wm, wn);
+        if (kk == NKK - 1 && has1) {
+          al.store(An, tid, ga);
+          bl.store(Bn, tid, gb);
         }
-        const int64_t k1 = (int64_t)(kt + 1) * BK;
-        const int64_t ka = (kt + 1) * a_step, kb = (kt + 1) * b_step;
-        al.load(make_rsrc(abase + ka, a_bytes - ka * 2), p.K - k1, tid);
-        bl.load(make_rsrc(bbase + kb, b_bytes - kb * 2), p.K - k1, tid);
-      }
-      mma_stage<T, DT>(lds + cur * T::STAGE, lds + cur * T::STAGE + T::A_CH, acc, lane, wm, wn);
-      if (more) {
-        al.store(lds + (cur ^ 1) * T::STAGE, tid);
-        bl.store(lds + (cur ^ 1) * T::STAGE + T::A_CH, tid);
+        mfmas<T, DT>(acc, fa[kk & 1], fb[kk & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
+      if (has1) read_frags<T>(An, Bn, 0, fa[0], fb[0], lane, wm, wn);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Epilogue: + bias in fp32, one RNE rounding to the 16-bit type, 8-byte stores. One
-  // 32x32 block at a time (scheduling fences keep the compiler from pulling every
-  // accumulator out of the AGPRs at once).
+  // Epilogue through LDS (the operand stages are free after the last barrier): each lane
+  // adds the bias in fp32, rounds once (RNE) and writes 4 consecutive outputs (8 bytes) of
+  // one row into a [BM][BN] 16-bit tile; then every thread copies 16-byte row chunks to
+  // global memory, a wave's lanes covering whole rows. 8-byte unit u of row r sits at unit
+  // u ^ (r & XM), so the 32 rows written by one instruction and the chunks of a row read
+  // back spread over the banks (XM keeps the unit inside its row for narrow tiles).
+  __syncthreads();  // the bias slice is visible even when the K loop ran no barrier (K == 0)
+  uint32_t* otile = reinterpret_cast<uint32_t*>(lds);
+  constexpr int ROW_U = BN / 4;  // 8-byte units per tile row
+  constexpr int XM = (ROW_U < 32 ? ROW_U : 32) - 1;
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
     const int ml = wm * T::WTM + fm * 32 + (lane & 31);
-    const bool row_ok = ml < rows_valid;
-    uint16_t* orow = p.out + (m0 + ml) * p.N + n0;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nl = wn * T::WTN + fn * 32 + g * 8 + (lane >> 5) * 4;
-        if (row_ok && nl < cols_valid) {
-          float x0 = acc[fm][fn][4 * g + 0], x1 = acc[fm][fn][4 * g + 1];
-          float x2 = acc[fm][fn][4 * g + 2], x3 = acc[fm][fn][4 * g + 3];
-          if (p.bias) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n0 + nl);
-            x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
-            x1 += Num<DT>::from_bits(bb[0] >> 16);
-            x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
-            x3 += Num<DT>::from_bits(bb[1] >> 16);
-          }
-          u32x2 o;
-          o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
-          o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
-          *reinterpret_cast<u32x2*>(orow + nl) = o;
+        float x0 = acc[fm][fn][4 * g + 0], x1 = acc[fm][fn][4 * g + 1];
+        float x2 = acc[fm][fn][4 * g + 2], x3 = acc[fm][fn][4 * g + 3];
+        if (p.bias) {
+          const u32x2 bb = bias_lds[nl >> 2];
+          x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
+          x1 += Num<DT>::from_bits(bb[0] >> 16);
+          x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
+          x3 += Num<DT>::from_bits(bb[1] >> 16);
         }
+        u32x2 o;
+        o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
+        o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
+        const int u = (nl >> 2) ^ (ml & XM);
+        *reinterpret_cast<u32x2*>(otile + (ml * ROW_U + u) * 2) = o;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __syncthreads();
+  constexpr int ROW_C = BN / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int c = tid; c < BM * ROW_C; c += kThreads) {
+    const int r = c / ROW_C, ch = c % ROW_C;
+    const int s = r & XM;
+    u32x4 v = *reinterpret_cast<const u32x4*>(otile + (r * ROW_U + (((2 * ch) ^ s) & ~1)) * 2);
+    if (s & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    if (r < rows_valid && ch * 8 < cols_valid)
+      *reinterpret_cast<u32x4*>(p.out + (m0 + r) * p.N + n0 + ch * 8) = v;
+  }
+  __syncthreads();  // the tile area is the next tile's stage 0
 }
 
 // Global row m of the gathered A; `shards` is the workgroup's LDS copy of the pointers.
@@ -430,14 +483,7 @@ __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards
     for (int j = 0; j < 8; ++j) v[j] = ld16(arow(p, shards, m_beg + mb * 8 + j) + k_beg + kb * 8);
     uint16_t* dst = p.staging + (k_beg + kb * 8) * p.M + m_beg + mb * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1, sh = (i & 1) * 16;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = ((v[2 * q][w] >> sh) & 0xffffu) | (((v[2 * q + 1][w] >> sh) & 0xffffu) << 16);
-      st16(dst + (int64_t)i * p.M, o);
-    }
+    for (int i = 0; i < 8; ++i) st16(dst + (int64_t)i * p.M, transpose_row(v, i));
   }
 }
 
@@ -464,15 +510,26 @@ __device__ void fetch_loop(const KParams& p, const uint16_t* const* shards, int 
   }
 }
 
+// Next tile for this workgroup, or -1: its XCD's queue first, then the other queues.
 __device__ inline int grab(const KParams& p) {
-  if (aborted(p)) return p.num_tiles;
-  return (int)atomicAdd(p.ctr + CTR_TILE, 1u);
+  if (aborted(p)) return -1;
+  const int x0 = (int)(blockIdx.x % kQueues);
+  for (int s = 0; s < kQueues; ++s) {
+    const int x = (x0 + s) % kQueues;
+    uint32_t* c = p.ctr + CTR_Q + x * CTR_QSTRIDE;
+    const uint32_t len = (uint32_t)p.qlen[x];
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const uint32_t i = atomicAdd(c, 1u);
+    if (i < len) return (int)p.qtiles[p.qoff[x] + (int)i];
+  }
+  return -1;
 }
 
 template <int BM, int DT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
   __shared__ u32x4 lds[2 * T::STAGE];
+  __shared__ u32x2 s_bias[T::BN / 4];
   __shared__ int s_next;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
@@ -484,11 +541,11 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     fetch_loop<T>(p, s_shards, wg, p.F, true, tr, tid);
   }
 
-  int nxt = 0;
+  int nxt = -1;
   if (tid == 0) s_next = grab(p);
   __syncthreads();
   int q = s_next;
-  while (q < p.num_tiles) {
+  while (q >= 0) {
     __syncthreads();  // everyone has read s_next
     if (tid == 0) nxt = grab(p);  // next tile's index travels while this one computes
     const int pos = q / p.T_n, t_n = q - pos * p.T_n;
@@ -497,12 +554,12 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, lds, tid, tr);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
     } else {
       if (!staged || p.staged_kmajor)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, lds, tid, tr);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, lds, tid, tr);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     if (tid == 0) s_next = nxt;
@@ -513,8 +570,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   if (tid == 0) {
     if (p.debug) p.trace_count[wg] = tr.n;
     const uint32_t old = atomicAdd(p.ctr + CTR_DONE, 1u);
-    if (old == gridDim.x - 1) {  // last workgroup out resets the queue for the next run
-      __hip_atomic_store(p.ctr + CTR_TILE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x - 1) {  // last workgroup out resets the queues for the next run
+      for (int x = 0; x < kQueues; ++x)
+        __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -160,6 +160,9 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg);
 #define AGMM_Q_STATUS 5       /* uint32[4]: {status, workgroup, flag index, value seen} */
 #define AGMM_Q_UNITS 6        /* uint32[2 * num_units]: (m-tile, k-group) in fetch order */
 #define AGMM_Q_MTILES 7       /* uint32[T_m]: m-tile in GEMM order, bit 31 = read in place */
+#define AGMM_Q_QUEUES 8       /* uint32[16 + num_tiles]: 8 queue offsets, 8 queue lengths, then
+                                 the tile ids queue by queue (tile id q = position of its
+                                 m-tile in GEMM order * T_n + n-tile) */
 
 /* Trace events (debug). One record per fetched unit, per computed tile and per flag wait
  * of wave 0, after the per-workgroup event ids of the iris issue (wg_fetch, wg_gemm,

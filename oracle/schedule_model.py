@@ -21,6 +21,9 @@ bit for bit:
   units      = for each window of Wm = max(1, ceil(W / T_n)) consecutive entries of S':
                  for g in 0..G-1: for t in window: (t, g)
   unit u  -> fetcher u mod F, each fetcher in increasing u
+  queues     = GEMM-order m-tiles in super-rows of 4; a super-row's tiles listed in column
+               blocks of 8 n-tiles (m-tile, then n, inside a block); super-row j appended
+               to queue j mod 8 (one queue per XCD); every tile in exactly one queue
   flags[t*G + g] == epoch after a run, for every staged unit; direct units untouched
   staging, k_contiguous:  S[m*K + k] = A[m][k];  m_contiguous: S[k*M + m] = A[m][k]
 """
@@ -91,6 +94,21 @@ def mtile_order(g: Geometry) -> List[int]:
 def gemm_tiles(g: Geometry) -> List[Tuple[int, int]]:
     """Tile q -> (t_m, t_n) in GEMM order."""
     return [(t, n) for t in mtile_order(g) for n in range(g.T_n)]
+
+
+N_QUEUES, SUPER_ROWS, COL_BLOCK = 8, 4, 8
+
+
+def tile_queues(g: Geometry) -> List[List[int]]:
+    """The per-XCD tile queues, as lists of tile ids q (q = GEMM position * T_n + n)."""
+    queues = [[] for _ in range(N_QUEUES)]
+    for j, s0 in enumerate(range(0, g.T_m, SUPER_ROWS)):
+        rows = range(s0, min(g.T_m, s0 + SUPER_ROWS))
+        for nb in range(0, g.T_n, COL_BLOCK):
+            for pos in rows:
+                for n in range(nb, min(g.T_n, nb + COL_BLOCK)):
+                    queues[j % N_QUEUES].append(pos * g.T_n + n)
+    return queues
 
 
 def fetch_units(g: Geometry) -> List[Tuple[int, int]]:

@@ -82,11 +82,13 @@ def test_validation_errors(A):
 
 
 def test_workspace_bytes_large(A):
-    # 16384x3584x8192, D=8, tile 256: staging M*K fp16, flags T_m*G, 56 staged m-tiles x 8
-    # k-groups of 8-byte unit records, 64 m-tile records, counters; 256-byte aligned pieces.
+    # 16384x3584x8192, D=8, tile 256: staging M*K fp16, flags T_m*G, counters (a done word,
+    # status words, 8 queue counters on their own 128-byte lines), 56 staged m-tiles x 8
+    # k-groups of 8-byte unit records, 64 m-tile records, 64*14 queue entries;
+    # 256-byte aligned pieces.
     al = lambda x: (x + 255) & ~255
-    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al(64 * 4) + al(56 * 8 * 8) + al(64 * 4)
-           + 0 + al(4))
+    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al((32 + 8 * 32) * 4) + al(56 * 8 * 8)
+           + al(64 * 4) + al(64 * 14 * 4) + 0 + al(4))
     got = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1)
     assert got == exp
     # direct_local off: all 64 m-tiles staged

@@ -43,6 +43,7 @@ def test_bookkeeping_matches_model(w, bm):
     g = geometry(w, cfg)
     # tables
     assert [tuple(u) for u in op.units()] == sm.fetch_units(g)
+    assert op.queues() == sm.tile_queues(g)
     mt = op.mtiles()
     assert [int(x & 0x7FFFFFFF) for x in mt] == sm.mtile_order(g)
     assert [bool(x >> 31) for x in mt] == [sm.is_direct(g, t) for t in sm.mtile_order(g)]
@@ -81,9 +82,12 @@ def test_bookkeeping_matches_model(w, bm):
                     assert not sm.is_direct(g, t_m)
                 else:
                     raise AssertionError(rec)
-            # a workgroup takes tiles in increasing queue order
+            # a workgroup takes tiles from each queue in that queue's order
             mine = [int(r["id"]) for r in recs[wg, :counts[wg]] if r["event"] == A.EV_GEMM]
-            assert mine == sorted(mine)
+            for qlist in sm.tile_queues(g):
+                posn = {t: i for i, t in enumerate(qlist)}
+                seq = [posn[t] for t in mine if t in posn]
+                assert seq == sorted(seq)
         assert [fetched[f] for f in range(g.F)] == sm.fetcher_lists(g)
         assert sorted(tiles) == list(range(len(sm.gemm_tiles(g))))
         assert np.array_equal(op.status(), np.zeros(4, dtype=np.uint32))

@@ -79,6 +79,9 @@ def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
         lists = sm.fetcher_lists(g)
         assert sorted(itertools.chain(*lists)) == list(range(len(units)))
         assert all(lst == sorted(lst) for lst in lists)
+    # queues partition the tiles
+    qs = sm.tile_queues(g)
+    assert sorted(itertools.chain(*qs)) == list(range(len(tiles)))
     # flags: exactly the staged units carry the epoch
     f = sm.expected_flags(g, 5)
     assert int((f == 5).sum()) == len(units)
@@ -96,3 +99,15 @@ def test_expected_staging_layouts():
     assert (k[:2] == 0xFFFF).all() and (k[2:] == A[2:]).all()
     m = sm.expected_staging(g, A, "m_contiguous", 0xFFFF).reshape(3, 4)
     assert (m[:, :2] == 0xFFFF).all() and (m[:, 2:] == A[2:].T).all()
+
+
+def test_queue_hand_example():
+    # T_m = 6 m-tiles (GEMM positions 0..5), T_n = 10: super-rows {0..3} -> queue 0,
+    # {4, 5} -> queue 1; column blocks of 8 then 2 n-tiles
+    g = geo(D=1, M=12, N=20, BM=2, BN=2)
+    assert (g.T_m, g.T_n) == (6, 10)
+    q = sm.tile_queues(g)
+    exp0 = [p * 10 + n for p in range(4) for n in range(8)] + \
+           [p * 10 + n for p in range(4) for n in range(8, 10)]
+    exp1 = [p * 10 + n for p in (4, 5) for n in range(8)] + [p * 10 + n for p in (4, 5) for n in (8, 9)]
+    assert q[0] == exp0 and q[1] == exp1 and all(not x for x in q[2:])
