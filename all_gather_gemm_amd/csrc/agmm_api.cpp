@@ -138,7 +138,7 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
     }
   }
   c.block_m = c.block_n = bm;
-  c.block_k = 16384 / bm;
+  c.block_k = agmm::kBlockK;
   c.k_per_flag = d.k_per_flag ? d.k_per_flag : std::max(1, 1024 / c.block_k);
   const int64_t KG = (int64_t)c.k_per_flag * c.block_k;
   const int64_t T_m = cdiv(d.M, bm), T_n = cdiv(d.N, bm);

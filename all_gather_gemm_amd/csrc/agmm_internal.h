@@ -9,6 +9,7 @@
 namespace agmm {
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
+constexpr int kBlockK = 32;    // K-tile depth of the GEMM worker (every tile family)
 
 // Output tiles are handed out from kQueues queues, one per XCD (workgroup w is placed on
 // XCD w % 8 by the dispatcher); a workgroup drains its own queue, then steals from the

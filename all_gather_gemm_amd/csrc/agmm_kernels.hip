@@ -9,13 +9,13 @@
 // benchmark", Kraken optimization) and the source choice is made once per tile, outside
 // the K loop (the same thread explains why a per-iteration choice defeats prefetching).
 //
-// GEMM worker: square output tiles BMxBM with BK = 16384/BM (256x256x64, 128x128x128,
-// 64x64x256), 4 wave64s in a 2x2 layout, v_mfma_f32_32x32x16_{f16,bf16} with fp32
-// accumulators, two LDS stages of 64 KiB (global loads for K-tile k+1 are in flight while
-// K-tile k is multiplied). LDS holds each operand as 16-byte chunks of 8 consecutive K
-// values ([K/8][MN] chunks, XOR-swizzled), the form the MFMA operands are read in; a
-// K-contiguous source is copied chunk for chunk, an MN-contiguous source (B, and A staged
-// m_contiguous) is transposed 8x8 in registers on its way into LDS.
+// GEMM worker: square output tiles BMxBM (256, 128 or 64), 4 wave64s in a 2x2 layout,
+// v_mfma_f32_32x32x16_{f16,bf16} with fp32 accumulators, K-tiles of 32 in four LDS stages.
+// Operand slices go global->LDS by buffer loads that write LDS directly, three K-tiles
+// ahead of use, so no registers hold data in flight; each operand keeps the layout it has
+// in memory (K-contiguous slices are read as 16-byte MFMA operands, MN-contiguous ones --
+// B, and A staged m_contiguous -- through the transposing ds_read_b64_tr_b16). One
+// barrier per K-tile; the output tile goes through LDS for 16-byte coalesced stores.
 //
 // Flag protocol: producer = every thread's agent-scope release fence (L2 write-back),
 // workgroup barrier, one agent-scope release store of the run's epoch. Consumer = relaxed
@@ -68,32 +68,38 @@ struct Num<AGMM_BF16> {
   }
 };
 
-// Tile family: square BMxBM output tile, BK = 16384/BM so that each operand's stage holds
-// 2048 16-byte chunks: 8 K-major chunks or one 8x8 MN-major block per thread.
-//
-// LDS layout of an operand stage: chunk (row r, K-chunk kc) -- 8 consecutive K values of
-// row r -- sits at kc * RS + phys(r), with the chunk-row stride RS = MN + 8 (8 chunks of
-// padding) and phys(r) = r ^ ((r>>3 ^ r>>6) & 7). The padding makes the K-chunk term
-// additive (each MFMA sub-step reads at a fixed offset from one base per lane); the XOR
-// spreads 8x8 transposed blocks. Checked exhaustively: MFMA operand reads, K-major stores
-// (8 rows x 8 K-chunks per wave instruction) and MN-major stores (16 blocks) hit distinct
-// 16-byte bank groups whether a 128-bit LDS access is served 8 or 16 lanes at a time.
+// Tile family: square BMxBM output tile (BM = 256, 128, 64), BK = 32, four LDS stages.
+// A stage holds the A and B slices of one K-tile, 4*BM 16-byte chunks each, in the layout
+// their source has in global memory, so both are copied global->LDS by buffer loads that
+// write LDS directly (no registers, no VALU):
+//  - a K-contiguous slice (A from a shard or k_contiguous staging) as [row][4 chunks], the
+//    chunk index XORed with g(row) = (row>>1 ^ row>>3) & 3; an MFMA operand is one 16-byte
+//    read per lane;
+//  - an MN-contiguous slice (B, or A from m_contiguous staging) as [k][MN/8 chunks], the
+//    chunk index XORed with f(k) = 4*(k%4) (4*((k>>1)%2) when a row has 8 chunks); an MFMA
+//    operand is two transposing 8-byte reads (ds_read_b64_tr_b16) per lane.
+// Checked on the CPU against the instruction's lane mapping (measured on the hardware):
+// every MFMA lane receives its elements and no 16-lane or 32-lane read pass has a bank
+// conflict; each DMA instruction fills 1 KiB of LDS linearly.
 template <int BM_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BM_, BK = 16384 / BM_;
-  static constexpr int KC = BK / 8;            // 16-byte K-chunks per row
-  static constexpr int RSA = BM + 8, RSB = BN + 8;
-  static constexpr int A_CH = KC * RSA;        // chunks per stage, A
-  static constexpr int B_CH = KC * RSB;        // chunks per stage, B
+  static constexpr int BM = BM_, BN = BM_, BK = kBlockK, NKK = BK / 16;
+  static_assert(BK == 32, "the LDS layouts below assume 32-deep K-tiles");
+  static constexpr int A_CH = BM * 4, B_CH = BN * 4;     // 16-byte chunks per stage
   static constexpr int STAGE = A_CH + B_CH;
+  static constexpr int ADMA = A_CH / 256, BDMA = B_CH / 256;  // DMA instructions per wave
+  static constexpr int DMA_PER_TILE = ADMA + BDMA;
   static constexpr int WTM = BM / 2, WTN = BN / 2;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static_assert(2 * STAGE * 16 >= BM * BN * 2, "epilogue tile fits in the stages");
+  static_assert(STAGE * 16 >= (BM / 4) * BN * 2, "an output quarter fits in a stage");
 };
 
-__device__ inline int phys(int r) { return r ^ (((r >> 3) ^ (r >> 6)) & 7); }
+__device__ inline int g_row(int m) { return ((m >> 1) ^ (m >> 3)) & 3; }
+template <int RC>
+__device__ inline int f_row(int k) { return RC >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 
 __device__ inline u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Row i of the transpose of an 8x8 block of 16-bit values held as 8 rows v[0..7] of four
 // dwords: element j of the result is element i of v[j]. v_perm_b32 picks two 16-bit halves
@@ -106,81 +112,102 @@ __device__ inline u32x4 transpose_row(const u32x4 (&v)[8], int i) {
   for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(v[2 * q + 1][w], v[2 * q][w], sel);
   return o;
 }
-__device__ inline void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Buffer resource over [base, base + bytes): loads at byte offsets at or past `bytes`
-// return zero, so a tile that runs past the end of its operand reads zeros without a
-// branch per load. The word 0x00020000 is the gfx9-family raw-buffer configuration.
+// Buffer resource over [base, base + bytes): accesses at byte offsets at or past `bytes`
+// read zero and touch no memory. The word 0x00020000 is the gfx9-family raw-buffer
+// configuration.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ inline rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffll ? 0xffffffffll : bytes);
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffll ? 0x7fffffffll : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0,
                                            (int)(uint32_t)n, 0x00020000);
 }
-__device__ inline u32x4 bload(rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource range used here
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16 bytes per lane from rs at voff into LDS at dst + 16 * lane (dst is wave-uniform):
+// buffer_load_dwordx4 ... lds, with the LDS base in M0. Written as inline asm so that the
+// compiler adds no waits of its own for it (it cannot tell which stage a DMA in flight
+// targets across the K loop's back edge and would drain every request); the K loop waits
+// for exactly the requests it needs with wait_vmcnt.
+__device__ inline void dma16(rsrc_t rs, const u32x4* dst, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(lds_void*)(const_cast<u32x4*>(dst)));
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0)
+               : "memory");
 }
 
-// K-contiguous operand tile (MN rows x BK), element (r, k) at base[r*ld + k]. Chunk
-// c = i*256 + tid is row (c / (8*KC))*8 + c % 8, K-chunk (c / 8) % KC: a wave instruction
-// covers 8 rows x 8 K-chunks (whole 128-byte row segments). A thread's K-chunk is the same
-// for every i and its row advances by 256/KC per i, so its byte offset is off0 + i*rstride.
-template <class T, int MN>
-struct KMajor {
-  static constexpr int PER = MN * T::KC / kThreads;
-  static constexpr int RPI = kThreads / T::KC;  // rows per i
-  typedef u32x4 Regs[PER];
-  uint32_t off0, rstride;
-  __device__ static inline int row0(int tid) { return (tid / (8 * T::KC)) * 8 + tid % 8; }
-  __device__ static inline int kchunk(int tid) { return (tid / 8) % T::KC; }
-  __device__ inline void init(int64_t ld, int tid) {
-    off0 = (uint32_t)((row0(tid) * ld + kchunk(tid) * 8) * 2);
-    rstride = (uint32_t)(RPI * ld * 2);
-  }
-  // rs covers the operand from column k0 onwards; k_rem = K - k0. Columns at or past K
-  // would read the next row, so the last K-tile of a ragged K is masked explicitly.
-  __device__ inline void load(rsrc_t rs, int64_t k_rem, int tid, Regs& v) const {
+// K-contiguous operand (rows x 32 K values per stage): element (r, k) at base[r*ld + k].
+// Wave w fills 1 KiB blocks b = w*NDMA + j of the slice: 16 rows x 4 chunks; lane i takes
+// row 16b + i/4, stored chunk slot i%4, i.e. source chunk (i%4) ^ g(row).
+template <int MN>
+struct KMajorDma {
+  static constexpr int NDMA = MN * 4 / 256;
+  uint32_t voff[NDMA];
+  int kc8[NDMA];  // first K column of the lane's chunk, relative to the stage's K offset
+  __device__ inline void init(int64_t ld, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = bload(rs, off0 + i * rstride);
-    if (k_rem < T::BK && kchunk(tid) * 8 >= k_rem) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) v[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < NDMA; ++j) {
+      const int b = wave * NDMA + j, row = 16 * b + lane / 4, c = (lane & 3) ^ g_row(row);
+      kc8[j] = 8 * c;
+      voff[j] = (uint32_t)((row * ld + 8 * c) * 2);
     }
   }
-  __device__ inline void store(u32x4* region, int tid, const Regs& v) const {
-    constexpr int RS = MN + 8;
-    u32x4* base = region + kchunk(tid) * RS;
-    const int r0 = row0(tid);
+  // rs covers the operand from column k0 onwards; k_rem = K - k0 (columns at or past K
+  // would read the next row: those lanes load from past the range instead, i.e. zeros).
+  __device__ inline void issue(rsrc_t rs, const u32x4* region, int wave, int64_t k_rem) const {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) base[phys(r0 + i * RPI)] = v[i];
+    for (int j = 0; j < NDMA; ++j)
+      dma16(rs, region + (wave * NDMA + j) * 64, kc8[j] < k_rem ? voff[j] : kOob);
+  }
+  // MFMA operand for rows rbase..rbase+31, K sub-step kk: lane l holds row rbase + l%32,
+  // K values 16*kk + 8*(l/32) .. +7.
+  __device__ static inline u32x4 frag(const u32x4* region, int rbase, int kk, int lane) {
+    const int row = rbase + (lane & 31), c = 2 * kk + (lane >> 5);
+    return region[row * 4 + (c ^ g_row(row))];
   }
 };
 
-// MN-contiguous operand tile (BK x MN), element (r, k) at base[k*ld + r]. Each thread moves
-// one 8x8 block: 8 rows of 8 MN-consecutive values in, 8 chunks of 8 K-consecutive out.
-// Rows at or past K lie past the operand's end (zeros); columns past the last valid one
-// read neighbouring data that only reaches output columns that are never stored.
-template <class T, int MN>
-struct MNMajor {
-  static constexpr int NBM = MN / 8;
-  static_assert(NBM * T::KC == kThreads, "one 8x8 block per thread");
-  typedef u32x4 Regs[8];
-  uint32_t off0, ld2;
-  __device__ inline void init(int64_t ld, int tid) {
-    const int nb = tid % NBM, kb = tid / NBM;
-    ld2 = (uint32_t)(ld * 2);
-    off0 = (uint32_t)((kb * 8 * ld + nb * 8) * 2);
-  }
-  __device__ inline void load(rsrc_t rs, int64_t /*k_rem*/, int /*tid*/, Regs& v) const {
+// MN-contiguous operand (32 K rows x MN per stage): element (r, k) at base[k*ld + r].
+// Block b covers chunks 64b .. 64b+63 of the [k][MN/8] slice; lane i stores chunk
+// q = 64b + i: row k = q / RC, slot q % RC, source chunk (q % RC) ^ f(k).
+template <int MN>
+struct MNMajorDma {
+  static constexpr int RC = MN / 8;   // chunks per row
+  static constexpr int NDMA = MN * 4 / 256;
+  static constexpr int ROWB = MN * 2; // bytes per LDS row
+  uint32_t voff[NDMA];
+  __device__ inline void init(int64_t ld, int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = bload(rs, off0 + j * ld2);
+    for (int j = 0; j < NDMA; ++j) {
+      const int q = (wave * NDMA + j) * 64 + lane, k = q / RC, c = (q % RC) ^ f_row<RC>(k);
+      voff[j] = (uint32_t)((k * ld + 8 * c) * 2);
+    }
   }
-  __device__ inline void store(u32x4* region, int tid, const Regs& v) const {
-    constexpr int RS = MN + 8;
-    const int nb = tid % NBM, kb = tid / NBM;
-    u32x4* base = region + kb * RS;
+  // Rows at or past K lie past the range (zeros); columns past the last valid one read
+  // neighbouring data that only reaches outputs that are never stored.
+  __device__ inline void issue(rsrc_t rs, const u32x4* region, int wave, int64_t) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) base[phys(nb * 8 + i)] = transpose_row(v, i);
+    for (int j = 0; j < NDMA; ++j) dma16(rs, region + (wave * NDMA + j) * 64, voff[j]);
+  }
+  // Byte offset, inside a stage slice, of this lane's half-0 transposing read for the
+  // operand block whose 32 MN positions start at mbase (K sub-step 0). The read for
+  // sub-step kk, half h is at +(16*kk + 4*h) * ROWB: f(k) depends only on the lane.
+  __device__ static inline int lane_off(int mbase, int lane) {
+    const int gidx = lane >> 4, s = lane & 15;
+    const int kl = 8 * (gidx >> 1) + (s >> 2);
+    const int mn = mbase + 16 * (gidx & 1) + 4 * (s & 3);
+    return kl * ROWB + (((mn >> 3) ^ f_row<RC>(kl)) * 16) + (mn & 7) * 2;
+  }
+  __device__ static inline u32x4 frag(const u32x4* region, int off, int kk) {
+    const char* p = reinterpret_cast<const char*>(region) + off + 16 * kk * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
   }
 };
 
@@ -240,22 +267,8 @@ __device__ inline void wait_flag(const KParams& p, int64_t idx, Tracer& tr) {
   tr.rec(AGMM_EV_GEMM_WAIT, (uint32_t)idx, v, polls, t0);
 }
 
-// MFMA operand fragments of sub-step kk (16 K values): lane l holds row (l % 32) of each
-// 32-row block, K values 8*(l / 32) .. +7.
-template <class T>
-__device__ inline void read_frags(const u32x4* As, const u32x4* Bs, int kk, u32x4 (&a)[T::FM],
-                                  u32x4 (&b)[T::FN], int lane, int wm, int wn) {
-  // lane-dependent part (K-chunk parity and row), then the sub-step as a constant offset
-  const u32x4* pa = As + (lane >> 5) * T::RSA + 2 * kk * T::RSA;
-  const u32x4* pb = Bs + (lane >> 5) * T::RSB + 2 * kk * T::RSB;
-#pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm) a[fm] = pa[phys(wm * T::WTM + fm * 32 + (lane & 31))];
-#pragma unroll
-  for (int fn = 0; fn < T::FN; ++fn) b[fn] = pb[phys(wn * T::WTN + fn * 32 + (lane & 31))];
-}
-
 // B is the MFMA's first operand, so each lane ends up holding 4 consecutive columns of one
-// output row (8-byte stores in the epilogue).
+// output row.
 template <class T, int DT>
 __device__ inline void mfmas(f32x16 (&acc)[T::FM][T::FN], const u32x4 (&a)[T::FM],
                              const u32x4 (&b)[T::FN]) {
@@ -265,18 +278,47 @@ __device__ inline void mfmas(f32x16 (&acc)[T::FM][T::FN], const u32x4 (&a)[T::FM
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = Num<DT>::mfma(b[fn], a[fm], acc[fm][fn]);
 }
 
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the K loop. __syncthreads() would also wait for every LDS DMA in
+// flight (its release fence counts them as pending LDS writes) and drain the prefetch; the
+// loop instead waits for exactly the DMA it needs (wait_vmcnt before this) and for its own
+// LDS reads, then meets at the hardware barrier. The empty asm and scheduling fences keep
+// the compiler from moving memory operations across it.
+__device__ inline void kloop_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// The four LDS stages, each its own array so that the compiler can tell a stage being
+// filled by DMA from the stage being read.
+template <class T>
+struct Stages {
+  u32x4* s[4];
+};
+
 // One output tile. A_KMAJOR: the A source is K-contiguous (local shard or k_contiguous
 // staging); otherwise it is the m_contiguous staging buffer. WAIT: fused mode, staged
-// k-groups are waited for before their first K-tile is loaded.
+// k-groups are waited for before their first K-tile is requested.
 //
-// Pipeline (K-tile t): at the top of step t the global loads of K-tile t+1 are issued into
-// registers; K-tile t is multiplied out of LDS stage t & 1 with the fragments of sub-step
-// kk+1 read while sub-step kk's MFMAs run; during the last sub-step the registers are
-// written (transposed where needed) into the other stage. One barrier per K-tile.
+// Pipeline over K-tiles t (stage t % 4): DMA requests run three K-tiles ahead. Step t:
+// read sub-step 1 fragments of t, run sub-step 0 MFMAs; wait for this wave's DMA of t+1
+// and meet at the barrier (after it, t+1 is in LDS for every wave and no wave reads stage
+// t any more); request t+4 into stage t % 4; read sub-step 0 fragments of t+1 and run
+// sub-step 1 MFMAs of t. One barrier per K-tile; fragments double buffered.
 template <class T, int DT, bool A_KMAJOR, bool WAIT>
-__device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4* lds,
+__device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const Stages<T>& st,
                           u32x2* bias_lds, int tid, Tracer& tr) {
-  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NKK = BK / 16;
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN;
   const int rows_valid = (int)min((int64_t)BM, p.M - m0);
@@ -304,81 +346,128 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4
   const int64_t b_bytes = (p.K * p.N - n0) * 2;
   const int64_t b_step = (int64_t)BK * p.N;
 
+  using ADma = typename std::conditional<A_KMAJOR, KMajorDma<BM>, MNMajorDma<BM>>::type;
+  using BDma = MNMajorDma<BN>;
+  ADma ad;
+  BDma bd;
+  ad.init(lda, wave, lane);
+  bd.init(p.N, wave, lane);
+
+  // fragment addressing (fixed per tile)
+  int aoff[T::FM], boff[T::FN];
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm)
+    aoff[fm] = A_KMAJOR ? 0 : MNMajorDma<BM>::lane_off(wm * T::WTM + fm * 32, lane);
+#pragma unroll
+  for (int fn = 0; fn < T::FN; ++fn) boff[fn] = BDma::lane_off(wn * T::WTN + fn * 32, lane);
+
+  auto read_frags = [&](const u32x4* stage, int kk, u32x4 (&a)[T::FM], u32x4 (&b)[T::FN]) {
+    const u32x4* As = stage;
+    const u32x4* Bs = stage + T::A_CH;
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm) {
+      if constexpr (A_KMAJOR)
+        a[fm] = KMajorDma<BM>::frag(As, wm * T::WTM + fm * 32, kk, lane);
+      else
+        a[fm] = MNMajorDma<BM>::frag(As, aoff[fm], kk);
+    }
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn) b[fn] = BDma::frag(Bs, boff[fn], kk);
+  };
+
   f32x16 acc[T::FM][T::FN];
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
 
-  using ALoad = typename std::conditional<A_KMAJOR, KMajor<T, BM>, MNMajor<T, BM>>::type;
-  using BLoad = MNMajor<T, BN>;
-  ALoad al;
-  BLoad bl;
-  al.init(lda, tid);
-  bl.init(p.N, tid);
-  typename ALoad::Regs ga;
-  typename BLoad::Regs gb;
-  u32x4 fa[2][T::FM], fb[2][T::FN];
-
   const int KT = (int)((p.K + BK - 1) / BK);
   const int64_t fbase = (int64_t)t_m * p.G;
   const bool waits = WAIT && staged;
+  const int kpf = p.kpf;
 
   // This tile's bias slice to LDS (read after the K loop's barriers).
   if (p.bias && tid < BN / 4)
     bias_lds[tid] = (n0 + tid * 4 < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n0 + tid * 4)
                                          : u32x2{0u, 0u};
 
-  // Issue the global loads of K-tile t, after its k-group's flag.
-  auto issue = [&](int t) {
-    if (waits && t % p.kpf == 0) wait_flag(p, fbase + t / p.kpf, tr);
+  // Request K-tile t into stage `dst`, after its k-group's flag.
+  auto request = [&](int t, const u32x4* dst) {
+    if (waits && t % kpf == 0) wait_flag(p, fbase + t / kpf, tr);
     const int64_t ka = t * a_step, kb = t * b_step;
-    al.load(make_rsrc(abase + ka, a_bytes - ka * 2), p.K - (int64_t)t * BK, tid, ga);
-    bl.load(make_rsrc(bbase + kb, b_bytes - kb * 2), 0, tid, gb);
+    ad.issue(make_rsrc(abase + ka, a_bytes - ka * 2), dst, wave, p.K - (int64_t)t * BK);
+    bd.issue(make_rsrc(bbase + kb, b_bytes - kb * 2), dst + T::A_CH, wave, 0);
+  };
+
+  u32x4 fa[2][T::FM], fb[2][T::FN];
+
+  // One K-tile step with compile-time stage index S (= t % 4).
+  auto step = [&](auto s_tag, int t) {
+    constexpr int S = decltype(s_tag)::value;
+    const u32x4* cur = st.s[S];
+    const u32x4* nxt = st.s[(S + 1) & 3];
+    read_frags(cur, 1, fa[1], fb[1]);
+    mfmas<T, DT>(acc, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // outstanding requests beyond t+1 that this wave may leave in flight
+    const int ahead = min(KT - 1, t + 3) - (t + 1);
+    if (ahead >= 2)
+      wait_vmcnt<2 * T::DMA_PER_TILE>();
+    else if (ahead == 1)
+      wait_vmcnt<T::DMA_PER_TILE>();
+    else
+      wait_vmcnt<0>();
+    kloop_barrier();
+    if (t + 4 < KT) request(t + 4, st.s[S]);
+    if (t + 1 < KT) read_frags(nxt, 0, fa[0], fb[0]);
+    mfmas<T, DT>(acc, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (KT > 0) {
-    issue(0);
-    al.store(lds, tid, ga);
-    bl.store(lds + T::A_CH, tid, gb);
-    __syncthreads();
-    read_frags<T>(lds, lds + T::A_CH, 0, fa[0], fb[0], lane, wm, wn);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      const u32x4* As = lds + cur * T::STAGE;
-      const u32x4* Bs = As + T::A_CH;
-      u32x4* An = lds + (cur ^ 1) * T::STAGE;
-      u32x4* Bn = An + T::A_CH;
-      const bool has1 = kt + 1 < KT;
-      if (has1) issue(kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK)
-          read_frags<T>(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], lane, wm, wn);
-        if (kk == NKK - 1 && has1) {
-          al.store(An, tid, ga);
-          bl.store(Bn, tid, gb);
-        }
-        mfmas<T, DT>(acc, fa[kk & 1], fb[kk & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
-      if (has1) read_frags<T>(An, Bn, 0, fa[0], fb[0], lane, wm, wn);
+    request(0, st.s[0]);
+    if (KT > 1) request(1, st.s[1]);
+    if (KT > 2) request(2, st.s[2]);
+    if (KT > 3) request(3, st.s[3]);
+    const int ahead0 = min(KT - 1, 3);
+    if (ahead0 >= 3)
+      wait_vmcnt<3 * T::DMA_PER_TILE>();
+    else if (ahead0 == 2)
+      wait_vmcnt<2 * T::DMA_PER_TILE>();
+    else if (ahead0 == 1)
+      wait_vmcnt<T::DMA_PER_TILE>();
+    else
+      wait_vmcnt<0>();
+    kloop_barrier();
+    read_frags(st.s[0], 0, fa[0], fb[0]);
+    int t = 0;
+    for (; t + 4 <= KT; t += 4) {
+      step(std::integral_constant<int, 0>{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+      step(std::integral_constant<int, 2>{}, t + 2);
+      step(std::integral_constant<int, 3>{}, t + 3);
     }
+    if (t < KT) step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < KT) step(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 < KT) step(std::integral_constant<int, 2>{}, t + 2);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Epilogue through LDS (the operand stages are free after the last barrier): each lane
-  // adds the bias in fp32, rounds once (RNE) and writes 4 consecutive outputs (8 bytes) of
-  // one row into a [BM][BN] 16-bit tile; then every thread copies 16-byte row chunks to
-  // global memory, a wave's lanes covering whole rows. 8-byte unit u of row r sits at unit
+  // Epilogue through LDS (all stages are free: every DMA has landed and the last barrier
+  // is behind every wave): each lane adds the bias in fp32, rounds once (RNE) and writes 4
+  // consecutive outputs (8 bytes) of one row into the output tile, whose row quarter
+  // q = r / (BM/4) lives in stage q; then every thread copies 16-byte row chunks to global
+  // memory, a wave's lanes covering whole rows. 8-byte unit u of row r sits at unit
   // u ^ (r & XM), so the 32 rows written by one instruction and the chunks of a row read
-  // back spread over the banks (XM keeps the unit inside its row for narrow tiles).
-  __syncthreads();  // the bias slice is visible even when the K loop ran no barrier (K == 0)
-  uint32_t* otile = reinterpret_cast<uint32_t*>(lds);
+  // back spread over the banks.
+  wait_vmcnt<0>();
+  __syncthreads();
   constexpr int ROW_U = BN / 4;  // 8-byte units per tile row
   constexpr int XM = (ROW_U < 32 ? ROW_U : 32) - 1;
+  constexpr int QR = BM / 4;     // rows per quarter
+  auto unit_ptr = [&](int r, int u) -> uint32_t* {
+    return reinterpret_cast<uint32_t*>(st.s[r / QR]) + ((r % QR) * ROW_U + u) * 2;
+  };
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
     const int ml = wm * T::WTM + fm * 32 + (lane & 31);
@@ -399,8 +488,7 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4
         u32x2 o;
         o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
         o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
-        const int u = (nl >> 2) ^ (ml & XM);
-        *reinterpret_cast<u32x2*>(otile + (ml * ROW_U + u) * 2) = o;
+        *reinterpret_cast<u32x2*>(unit_ptr(ml, (nl >> 2) ^ (ml & XM))) = o;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -411,12 +499,12 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, u32x4
   for (int c = tid; c < BM * ROW_C; c += kThreads) {
     const int r = c / ROW_C, ch = c % ROW_C;
     const int s = r & XM;
-    u32x4 v = *reinterpret_cast<const u32x4*>(otile + (r * ROW_U + (((2 * ch) ^ s) & ~1)) * 2);
+    u32x4 v = *reinterpret_cast<const u32x4*>(unit_ptr(r, ((2 * ch) ^ s) & ~1));
     if (s & 1) v = u32x4{v[2], v[3], v[0], v[1]};
     if (r < rows_valid && ch * 8 < cols_valid)
       *reinterpret_cast<u32x4*>(p.out + (m0 + r) * p.N + n0 + ch * 8) = v;
   }
-  __syncthreads();  // the tile area is the next tile's stage 0
+  __syncthreads();  // the tile area is the next tile's stages
 }
 
 // Global row m of the gathered A; `shards` is the workgroup's LDS copy of the pointers.
@@ -528,8 +616,13 @@ __device__ inline int grab(const KParams& p) {
 template <int BM, int DT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
-  __shared__ u32x4 lds[2 * T::STAGE];
+  __shared__ u32x4 lds0[T::STAGE], lds1[T::STAGE], lds2[T::STAGE], lds3[T::STAGE];
   __shared__ u32x2 s_bias[T::BN / 4];
+  Stages<T> st;
+  st.s[0] = lds0;
+  st.s[1] = lds1;
+  st.s[2] = lds2;
+  st.s[3] = lds3;
   __shared__ int s_next;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
@@ -554,12 +647,12 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, st, s_bias, tid, tr);
     } else {
       if (!staged || p.staged_kmajor)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, lds, s_bias, tid, tr);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, st, s_bias, tid, tr);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     if (tid == 0) s_next = nxt;
