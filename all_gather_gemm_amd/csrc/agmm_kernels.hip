@@ -117,10 +117,18 @@ __device__ inline u32x4 transpose_row(const u32x4 (&v)[8], int i) {
 // read zero and touch no memory. The word 0x00020000 is the gfx9-family raw-buffer
 // configuration.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Callers pass workgroup-uniform values; readfirstlane states that, so the descriptor
+// lives in SGPRs as the buffer instructions require.
+__device__ inline uint32_t uniform32(uint32_t x) {
+  // the builtin returns a signed int: go back to 32 unsigned bits before any widening
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
 __device__ inline rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffffll ? 0x7fffffffll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0,
-                                           (int)(uint32_t)n, 0x00020000);
+  const uint64_t a = (uint64_t)(size_t)base;
+  const uint64_t au = (uint64_t)uniform32((uint32_t)a) | ((uint64_t)uniform32((uint32_t)(a >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(au), (short)0,
+                                           (int)uniform32((uint32_t)n), 0x00020000);
 }
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource range used here
 
@@ -128,14 +136,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16 bytes per lane from rs at voff into LDS at dst + 16 * lane (dst is wave-uniform):
-// buffer_load_dwordx4 ... lds, with the LDS base in M0. Written as inline asm so that the
-// compiler adds no waits of its own for it (it cannot tell which stage a DMA in flight
-// targets across the K loop's back edge and would drain every request); the K loop waits
-// for exactly the requests it needs with wait_vmcnt.
-__device__ inline void dma16(rsrc_t rs, const u32x4* dst, uint32_t voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(size_t)(lds_void*)(const_cast<u32x4*>(dst)));
+// 16 bytes per lane from rs at voff into LDS at byte address m0 + 16 * lane (m0 is
+// wave-uniform): buffer_load_dwordx4 ... lds, with the LDS base in M0. Written as inline
+// asm so that the compiler adds no waits of its own for it (it cannot tell which stage a
+// DMA in flight targets across the K loop's back edge and would drain every request); the
+// K loop waits for exactly the requests it needs with wait_vmcnt.
+__device__ inline void dma16(rsrc_t rs, uint32_t m0, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0)
                : "memory");
 }
@@ -156,12 +162,12 @@ struct KMajorDma {
       voff[j] = (uint32_t)((row * ld + 8 * c) * 2);
     }
   }
-  // rs covers the operand from column k0 onwards; k_rem = K - k0 (columns at or past K
-  // would read the next row: those lanes load from past the range instead, i.e. zeros).
-  __device__ inline void issue(rsrc_t rs, const u32x4* region, int wave, int64_t k_rem) const {
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j)
-      dma16(rs, region + (wave * NDMA + j) * 64, kc8[j] < k_rem ? voff[j] : kOob);
+  // DMA j of this wave; rs covers the operand from column k0 onwards, k_rem = K - k0
+  // (columns at or past K would read the next row: those lanes load from past the range
+  // instead, i.e. zeros); region = LDS byte address of the slice, wave wave-uniform.
+  __device__ inline void issue(int j, rsrc_t rs, uint32_t region, uint32_t wave,
+                               int64_t k_rem) const {
+    dma16(rs, region + (wave * NDMA + j) * 1024u, kc8[j] < k_rem ? voff[j] : kOob);
   }
   // MFMA operand for rows rbase..rbase+31, K sub-step kk: lane l holds row rbase + l%32,
   // K values 16*kk + 8*(l/32) .. +7.
@@ -187,11 +193,10 @@ struct MNMajorDma {
       voff[j] = (uint32_t)((k * ld + 8 * c) * 2);
     }
   }
-  // Rows at or past K lie past the range (zeros); columns past the last valid one read
-  // neighbouring data that only reaches outputs that are never stored.
-  __device__ inline void issue(rsrc_t rs, const u32x4* region, int wave, int64_t) const {
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma16(rs, region + (wave * NDMA + j) * 64, voff[j]);
+  // DMA j of this wave. Rows at or past K lie past the range (zeros); columns past the
+  // last valid one read neighbouring data that only reaches outputs that are never stored.
+  __device__ inline void issue(int j, rsrc_t rs, uint32_t region, uint32_t wave, int64_t) const {
+    dma16(rs, region + (wave * NDMA + j) * 1024u, voff[j]);
   }
   // Byte offset, inside a stage slice, of this lane's half-0 transposing read for the
   // operand block whose 32 MN positions start at mbase (K sub-step 0). The read for
@@ -300,11 +305,19 @@ __device__ inline void kloop_barrier() {
 }
 
 // The four LDS stages, each its own array so that the compiler can tell a stage being
-// filled by DMA from the stage being read.
+// filled by DMA from the stage being read; off[] are their LDS byte addresses (uniform).
 template <class T>
 struct Stages {
   u32x4* s[4];
+  uint32_t off[4];
 };
+
+// Issue slot of item i of n spread over the m MFMAs of a half step: item i goes after MFMA
+// slot(i) (shift 0) or half a spacing later (shift 1), so that DMA requests and fragment
+// reads interleave with the MFMAs instead of queueing behind each other.
+__host__ __device__ constexpr int spread(int i, int n, int m, int shift) {
+  return n <= 0 ? 0 : ((2 * i + shift) * m / (2 * n) < m ? (2 * i + shift) * m / (2 * n) : m - 1);
+}
 
 // One output tile. A_KMAJOR: the A source is K-contiguous (local shard or k_contiguous
 // staging); otherwise it is the m_contiguous staging buffer. WAIT: fused mode, staged
@@ -316,7 +329,7 @@ struct Stages {
 // t any more); request t+4 into stage t % 4; read sub-step 0 fragments of t+1 and run
 // sub-step 1 MFMAs of t. One barrier per K-tile; fragments double buffered.
 template <class T, int DT, bool A_KMAJOR, bool WAIT>
-__device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const Stages<T>& st,
+__device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const Stages<T>& st,
                           u32x2* bias_lds, int tid, Tracer& tr) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -361,20 +374,6 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const
 #pragma unroll
   for (int fn = 0; fn < T::FN; ++fn) boff[fn] = BDma::lane_off(wn * T::WTN + fn * 32, lane);
 
-  auto read_frags = [&](const u32x4* stage, int kk, u32x4 (&a)[T::FM], u32x4 (&b)[T::FN]) {
-    const u32x4* As = stage;
-    const u32x4* Bs = stage + T::A_CH;
-#pragma unroll
-    for (int fm = 0; fm < T::FM; ++fm) {
-      if constexpr (A_KMAJOR)
-        a[fm] = KMajorDma<BM>::frag(As, wm * T::WTM + fm * 32, kk, lane);
-      else
-        a[fm] = MNMajorDma<BM>::frag(As, aoff[fm], kk);
-    }
-#pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) b[fn] = BDma::frag(Bs, boff[fn], kk);
-  };
-
   f32x16 acc[T::FM][T::FN];
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm)
@@ -391,65 +390,143 @@ __device__ void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const
     bias_lds[tid] = (n0 + tid * 4 < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n0 + tid * 4)
                                          : u32x2{0u, 0u};
 
-  // Request K-tile t into stage `dst`, after its k-group's flag.
-  auto request = [&](int t, const u32x4* dst) {
-    if (waits && t % kpf == 0) wait_flag(p, fbase + t / kpf, tr);
-    const int64_t ka = t * a_step, kb = t * b_step;
-    ad.issue(make_rsrc(abase + ka, a_bytes - ka * 2), dst, wave, p.K - (int64_t)t * BK);
-    bd.issue(make_rsrc(bbase + kb, b_bytes - kb * 2), dst + T::A_CH, wave, 0);
+  // Request K-tile t: the flag wait (fused mode, first K-tile of a staged k-group) and the
+  // buffer resources; the DMA instructions themselves are issued one by one, between MFMAs.
+  struct Req {
+    rsrc_t ra, rb;
+    int64_t k_rem;
   };
+  // Fused mode: wait for every staged k-group whose first K-tile lies in [lo, hi]. Called
+  // once per block of four K-tiles, before the block that requests them, so the polling
+  // code stays outside the unrolled MFMA stream.
+  auto wait_range = [&](int lo, int hi) {
+    if (!waits) return;
+    for (int g = (lo + kpf - 1) / kpf; g * kpf <= hi; ++g) wait_flag(p, fbase + g, tr);
+  };
+  auto resources = [&](int t) -> Req {
+    const int64_t ka = t * a_step, kb = t * b_step;
+    return Req{make_rsrc(abase + ka, a_bytes - ka * 2), make_rsrc(bbase + kb, b_bytes - kb * 2),
+               p.K - (int64_t)t * BK};
+  };
+  const uint32_t wave_u = uniform32((uint32_t)wave);
+  auto issue = [&](int d, const Req& r, uint32_t stage_off) {
+    if (d < T::ADMA)
+      ad.issue(d, r.ra, stage_off, wave_u, r.k_rem);
+    else
+      bd.issue(d - T::ADMA, r.rb, stage_off + T::A_CH * 16, wave_u, 0);
+  };
+  auto request = [&](int t, uint32_t stage_off) {
+    const Req r = resources(t);
+#pragma unroll
+    for (int d = 0; d < T::DMA_PER_TILE; ++d) issue(d, r, stage_off);
+  };
+  // Fragment read number i of a half step: A operands first, then B.
+  auto read_one = [&](int i, const u32x4* stage, int kk, u32x4 (&a)[T::FM], u32x4 (&b)[T::FN]) {
+    if (i < T::FM) {
+      if constexpr (A_KMAJOR)
+        a[i] = KMajorDma<BM>::frag(stage, wm * T::WTM + i * 32, kk, lane);
+      else
+        a[i] = MNMajorDma<BM>::frag(stage, aoff[i], kk);
+    } else {
+      b[i - T::FM] = BDma::frag(stage + T::A_CH, boff[i - T::FM], kk);
+    }
+  };
+  constexpr int NM = T::FM * T::FN, NR = T::FM + T::FN, ND = T::DMA_PER_TILE;
 
   u32x4 fa[2][T::FM], fb[2][T::FN];
 
-  // One K-tile step with compile-time stage index S (= t % 4).
-  auto step = [&](auto s_tag, int t) {
+  // One K-tile step with compile-time stage index S (= t % 4). FULL: t + 4 < KT, so the
+  // step requests t + 4, reads t + 1 and leaves two K-tiles of requests in flight.
+  auto step = [&](auto s_tag, auto full_tag, int t) {
     constexpr int S = decltype(s_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
     const u32x4* cur = st.s[S];
     const u32x4* nxt = st.s[(S + 1) & 3];
-    read_frags(cur, 1, fa[1], fb[1]);
-    mfmas<T, DT>(acc, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
+    // part 1: sub-step 0 MFMAs of t, sub-step 1 fragments of t read in between
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int fm = i / T::FN, fn = i % T::FN;
+      acc[fm][fn] = Num<DT>::mfma(fb[0][fn], fa[0][fm], acc[fm][fn]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if (spread(r, NR, NM, 0) == i) read_one(r, cur, 1, fa[1], fb[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // outstanding requests beyond t+1 that this wave may leave in flight
-    const int ahead = min(KT - 1, t + 3) - (t + 1);
+    const int ahead = FULL ? 2 : min(KT - 1, t + 3) - (t + 1);
     if (ahead >= 2)
-      wait_vmcnt<2 * T::DMA_PER_TILE>();
+      wait_vmcnt<2 * ND>();
     else if (ahead == 1)
-      wait_vmcnt<T::DMA_PER_TILE>();
+      wait_vmcnt<ND>();
     else
       wait_vmcnt<0>();
     kloop_barrier();
-    if (t + 4 < KT) request(t + 4, st.s[S]);
-    if (t + 1 < KT) read_frags(nxt, 0, fa[0], fb[0]);
-    mfmas<T, DT>(acc, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
+    // part 2: sub-step 1 MFMAs of t; requests of t + 4 into stage S and sub-step 0
+    // fragments of t + 1 in between
+    const bool do_req = FULL || t + 4 < KT;
+    const bool do_read = FULL || t + 1 < KT;
+    const Req rq = resources(t + 4);  // plain arithmetic, also past the last K-tile
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int fm = i / T::FN, fn = i % T::FN;
+      acc[fm][fn] = Num<DT>::mfma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+      if (do_req) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+          if (spread(d, ND, NM, 0) == i) issue(d, rq, st.off[S]);
+      }
+      if (do_read) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (spread(r, NR, NM, 1) == i) read_one(r, nxt, 0, fa[0], fb[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using YES = std::true_type;
+  using NO = std::false_type;
 
   if (KT > 0) {
-    request(0, st.s[0]);
-    if (KT > 1) request(1, st.s[1]);
-    if (KT > 2) request(2, st.s[2]);
-    if (KT > 3) request(3, st.s[3]);
+    wait_range(0, min(KT - 1, 3));
+    request(0, st.off[0]);
+    if (KT > 1) request(1, st.off[1]);
+    if (KT > 2) request(2, st.off[2]);
+    if (KT > 3) request(3, st.off[3]);
     const int ahead0 = min(KT - 1, 3);
     if (ahead0 >= 3)
-      wait_vmcnt<3 * T::DMA_PER_TILE>();
+      wait_vmcnt<3 * ND>();
     else if (ahead0 == 2)
-      wait_vmcnt<2 * T::DMA_PER_TILE>();
+      wait_vmcnt<2 * ND>();
     else if (ahead0 == 1)
-      wait_vmcnt<T::DMA_PER_TILE>();
+      wait_vmcnt<ND>();
     else
       wait_vmcnt<0>();
     kloop_barrier();
-    read_frags(st.s[0], 0, fa[0], fb[0]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_one(r, st.s[0], 0, fa[0], fb[0]);
     int t = 0;
-    for (; t + 4 <= KT; t += 4) {
-      step(std::integral_constant<int, 0>{}, t);
-      step(std::integral_constant<int, 1>{}, t + 1);
-      step(std::integral_constant<int, 2>{}, t + 2);
-      step(std::integral_constant<int, 3>{}, t + 3);
+    for (; t + 8 <= KT; t += 4) {
+      wait_range(t + 4, t + 7);
+      step(I0{}, YES{}, t);
+      step(I1{}, YES{}, t + 1);
+      step(I2{}, YES{}, t + 2);
+      step(I3{}, YES{}, t + 3);
     }
-    if (t < KT) step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < KT) step(std::integral_constant<int, 1>{}, t + 1);
-    if (t + 2 < KT) step(std::integral_constant<int, 2>{}, t + 2);
+    if (t + 4 <= KT) {
+      wait_range(t + 4, KT - 1);
+      step(I0{}, NO{}, t);
+      step(I1{}, NO{}, t + 1);
+      step(I2{}, NO{}, t + 2);
+      step(I3{}, NO{}, t + 3);
+      t += 4;
+    }
+    if (t < KT) step(I0{}, NO{}, t);
+    if (t + 1 < KT) step(I1{}, NO{}, t + 1);
+    if (t + 2 < KT) step(I2{}, NO{}, t + 2);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -623,6 +700,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   st.s[1] = lds1;
   st.s[2] = lds2;
   st.s[3] = lds3;
+  st.off[0] = (uint32_t)(size_t)(lds_void*)lds0;
+  st.off[1] = (uint32_t)(size_t)(lds_void*)lds1;
+  st.off[2] = (uint32_t)(size_t)(lds_void*)lds2;
+  st.off[3] = (uint32_t)(size_t)(lds_void*)lds3;
   __shared__ int s_next;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
@@ -637,7 +718,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   int nxt = -1;
   if (tid == 0) s_next = grab(p);
   __syncthreads();
-  int q = s_next;
+  int q = __builtin_amdgcn_readfirstlane(s_next);  // uniform: tile addressing in SGPRs
   while (q >= 0) {
     __syncthreads();  // everyone has read s_next
     if (tid == 0) nxt = grab(p);  // next tile's index travels while this one computes
@@ -657,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     if (tid == 0) s_next = nxt;
     __syncthreads();
-    q = s_next;
+    q = __builtin_amdgcn_readfirstlane(s_next);
   }
 
   if (tid == 0) {
