@@ -283,6 +283,15 @@ __device__ inline void mfmas(f32x16 (&acc)[T::FM][T::FN], const u32x4 (&a)[T::FM
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = Num<DT>::mfma(b[fn], a[fm], acc[fm][fn]);
 }
 
+// One accumulator element, copied out of its AGPR where it is used. Left to itself the
+// register allocator moves every accumulator into VGPRs at the end of the K loop, which
+// does not fit and spills.
+__device__ inline float acc_read(const f32x16& v, int i) {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v[i]));
+  return x;
+}
+
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -382,13 +391,30 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 
   const int KT = (int)((p.K + BK - 1) / BK);
   const int64_t fbase = (int64_t)t_m * p.G;
-  const bool waits = WAIT && staged;
+  bool waits = WAIT && staged;
   const int kpf = p.kpf;
+  // A poll inside the K loop drains this wave's DMA requests in flight (vector loads
+  // complete in order), so first look at every k-group's flag while the pipeline is still
+  // empty: when all are published already (the usual case once the fetchers are ahead),
+  // one acquire covers the whole tile and the K loop polls nothing.
+  if (waits) {
+    bool all = true;
+    for (int g = 0; g < p.G && all; ++g)
+      all = uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT)) == p.epoch;
+    if (all) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      waits = false;
+    }
+  }
 
   // This tile's bias slice to LDS (read after the K loop's barriers).
-  if (p.bias && tid < BN / 4)
-    bias_lds[tid] = (n0 + tid * 4 < p.N) ? *reinterpret_cast<const u32x2*>(p.bias + n0 + tid * 4)
-                                         : u32x2{0u, 0u};
+  // (zeros without a bias: the epilogue then has no branch, which would otherwise make the
+  // compiler move every accumulator out of the AGPRs at once and spill)
+  if (tid < BN / 4)
+    bias_lds[tid] = (p.bias && n0 + tid * 4 < p.N)
+                        ? *reinterpret_cast<const u32x2*>(p.bias + n0 + tid * 4)
+                        : u32x2{0u, 0u};
 
   // Request K-tile t: the flag wait (fused mode, first K-tile of a staged k-group) and the
   // buffer resources; the DMA instructions themselves are issued one by one, between MFMAs.
@@ -435,14 +461,20 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 
   u32x4 fa[2][T::FM], fb[2][T::FN];
 
-  // One K-tile step with compile-time stage index S (= t % 4). FULL: t + 4 < KT, so the
-  // step requests t + 4, reads t + 1 and leaves two K-tiles of requests in flight.
+  // One K-tile step with compile-time stage index S (= t % 4). FULL: t + 4 < KT, so every
+  // request below exists. The DMA of a K-tile is issued in two halves one step apart: its
+  // A slice in part 2 of step t - 4 (the step that frees the stage), its B slice in part 1
+  // of step t - 3, so the texture path and the LDS see a steady stream of requests over
+  // the whole step instead of a burst after each barrier.
   auto step = [&](auto s_tag, auto full_tag, int t) {
     constexpr int S = decltype(s_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
     const u32x4* cur = st.s[S];
     const u32x4* nxt = st.s[(S + 1) & 3];
-    // part 1: sub-step 0 MFMAs of t, sub-step 1 fragments of t read in between
+    // part 1: sub-step 0 MFMAs of t; sub-step 1 fragments of t and the B slice of t + 3
+    // (into the stage of t - 1, free since the last barrier) in between
+    const bool do_req1 = FULL || t + 3 < KT;
+    const Req rq1 = resources(t + 3);  // plain arithmetic, also past the last K-tile
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int fm = i / T::FN, fn = i % T::FN;
@@ -450,9 +482,15 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         if (spread(r, NR, NM, 0) == i) read_one(r, cur, 1, fa[1], fb[1]);
+      if (do_req1) {
+#pragma unroll
+        for (int d = 0; d < T::BDMA; ++d)
+          if (spread(d, T::BDMA, NM, 1) == i) issue(T::ADMA + d, rq1, st.off[(S + 3) & 3]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // outstanding requests beyond t+1 that this wave may leave in flight
+    // requests issued after the last one of t + 1, which this wave may leave in flight:
+    // those of t + 2 and t + 3 that exist
     const int ahead = FULL ? 2 : min(KT - 1, t + 3) - (t + 1);
     if (ahead >= 2)
       wait_vmcnt<2 * ND>();
@@ -461,19 +499,19 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     else
       wait_vmcnt<0>();
     kloop_barrier();
-    // part 2: sub-step 1 MFMAs of t; requests of t + 4 into stage S and sub-step 0
+    // part 2: sub-step 1 MFMAs of t; the A slice of t + 4 into stage S and sub-step 0
     // fragments of t + 1 in between
     const bool do_req = FULL || t + 4 < KT;
     const bool do_read = FULL || t + 1 < KT;
-    const Req rq = resources(t + 4);  // plain arithmetic, also past the last K-tile
+    const Req rq = resources(t + 4);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int fm = i / T::FN, fn = i % T::FN;
       acc[fm][fn] = Num<DT>::mfma(fb[1][fn], fa[1][fm], acc[fm][fn]);
       if (do_req) {
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
-          if (spread(d, ND, NM, 0) == i) issue(d, rq, st.off[S]);
+        for (int d = 0; d < T::ADMA; ++d)
+          if (spread(d, T::ADMA, NM, 0) == i) issue(d, rq, st.off[S]);
       }
       if (do_read) {
 #pragma unroll
@@ -495,10 +533,14 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     request(0, st.off[0]);
     if (KT > 1) request(1, st.off[1]);
     if (KT > 2) request(2, st.off[2]);
-    if (KT > 3) request(3, st.off[3]);
+    if (KT > 3) {  // the A slice only: step 0 requests the B slice
+      const Req r = resources(3);
+#pragma unroll
+      for (int d = 0; d < T::ADMA; ++d) issue(d, r, st.off[3]);
+    }
     const int ahead0 = min(KT - 1, 3);
     if (ahead0 >= 3)
-      wait_vmcnt<3 * ND>();
+      wait_vmcnt<2 * ND + T::ADMA>();
     else if (ahead0 == 2)
       wait_vmcnt<2 * ND>();
     else if (ahead0 == 1)
@@ -553,15 +595,13 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int nl = wn * T::WTN + fn * 32 + g * 8 + (lane >> 5) * 4;
-        float x0 = acc[fm][fn][4 * g + 0], x1 = acc[fm][fn][4 * g + 1];
-        float x2 = acc[fm][fn][4 * g + 2], x3 = acc[fm][fn][4 * g + 3];
-        if (p.bias) {
-          const u32x2 bb = bias_lds[nl >> 2];
-          x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
-          x1 += Num<DT>::from_bits(bb[0] >> 16);
-          x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
-          x3 += Num<DT>::from_bits(bb[1] >> 16);
-        }
+        float x0 = acc_read(acc[fm][fn], 4 * g + 0), x1 = acc_read(acc[fm][fn], 4 * g + 1);
+        float x2 = acc_read(acc[fm][fn], 4 * g + 2), x3 = acc_read(acc[fm][fn], 4 * g + 3);
+        const u32x2 bb = bias_lds[nl >> 2];
+        x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
+        x1 += Num<DT>::from_bits(bb[0] >> 16);
+        x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
+        x3 += Num<DT>::from_bits(bb[1] >> 16);
         u32x2 o;
         o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
         o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);

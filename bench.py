@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--fetch-wgs", type=int, default=0)
     ap.add_argument("--k-per-flag", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times): the "
+                         "known-size reference for the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,6 +142,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                          "dispatches": 3}), flush=True)
+        return
     tun = {}
     if args.block_m:
         tun["block_m"] = args.block_m
