@@ -337,9 +337,15 @@ __host__ __device__ constexpr int spread(int i, int n, int m, int shift) {
 // and meet at the barrier (after it, t+1 is in LDS for every wave and no wave reads stage
 // t any more); request t+4 into stage t % 4; read sub-step 0 fragments of t+1 and run
 // sub-step 1 MFMAs of t. One barrier per K-tile; fragments double buffered.
+__device__ inline int grab(const KParams& p);
+
+// next_tile: thread 0 stores the workgroup's next tile index there once this tile's K loop
+// is done, so the queue atomic's round trip overlaps the epilogue while no tile is claimed
+// long before it can start (claiming at the start of a tile lets the first workgroups to
+// arrive take two tiles each and starve the rest when tiles and workgroups are few).
 template <class T, int DT, bool A_KMAJOR, bool WAIT>
 __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const Stages<T>& st,
-                          u32x2* bias_lds, int tid, Tracer& tr) {
+                          u32x2* bias_lds, int tid, Tracer& tr, int* next_tile) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN;
@@ -571,6 +577,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     if (t + 2 < KT) step(I2{}, NO{}, t + 2);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if (tid == 0) *next_tile = grab(p);
 
   // Epilogue through LDS (all stages are free: every DMA has landed and the last barrier
   // is behind every wave): each lane adds the bias in fp32, rounds once (RNE) and writes 4
@@ -723,7 +730,9 @@ __device__ inline int grab(const KParams& p) {
     const int x = (x0 + s) % kQueues;
     uint32_t* c = p.ctr + CTR_Q + x * CTR_QSTRIDE;
     const uint32_t len = (uint32_t)p.qlen[x];
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    if (len == 0) continue;
+    // Always the read-modify-write: a plain load of another XCD's queue counter can return a
+    // stale "exhausted" value and send the workgroup away while tiles are left.
     const uint32_t i = atomicAdd(c, 1u);
     if (i < len) return (int)p.qtiles[p.qoff[x] + (int)i];
   }
@@ -755,28 +764,25 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     fetch_loop<T>(p, s_shards, wg, p.F, true, tr, tid);
   }
 
-  int nxt = -1;
   if (tid == 0) s_next = grab(p);
   __syncthreads();
   int q = __builtin_amdgcn_readfirstlane(s_next);  // uniform: tile addressing in SGPRs
   while (q >= 0) {
     __syncthreads();  // everyone has read s_next
-    if (tid == 0) nxt = grab(p);  // next tile's index travels while this one computes
     const int pos = q / p.T_n, t_n = q - pos * p.T_n;
     const uint32_t e = p.mtiles[pos];
     const int t_m = (int)(e & 0x7fffffffu);
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, st, s_bias, tid, tr);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
     } else {
       if (!staged || p.staged_kmajor)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, st, s_bias, tid, tr);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
-    if (tid == 0) s_next = nxt;
     __syncthreads();
     q = __builtin_amdgcn_readfirstlane(s_next);
   }
