@@ -644,7 +644,11 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
   __syncthreads();
 }
 
-// Copy unit (t_m, g) into k_contiguous staging: 16-byte loads and stores, 8 in flight.
+// A fetcher workgroup keeps 128 KiB of loads in flight (32 x 16 bytes per thread): one
+// workgroup's copy rate is bound by latency, not by its share of the HBM bandwidth.
+constexpr int kFetchDepth = 32;
+
+// Copy unit (t_m, g) into k_contiguous staging: 16-byte loads, then 16-byte stores.
 template <int BM>
 __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid) {
@@ -653,61 +657,76 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
   const int64_t k_beg = (int64_t)g * KG;
   const int CR = (int)(min((int64_t)KG, p.K - k_beg) / 8);
   const int total = R * CR;
-  for (int base = 0; base < total; base += kThreads * 8) {
-    u32x4 v[8];
-    int64_t dst[8];
+  for (int base = 0; base < total; base += kThreads * kFetchDepth) {
+    u32x4 v[kFetchDepth];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kFetchDepth; ++i) {
       const int c = base + i * kThreads + tid;
       if (c < total) {
         const int r = c / CR, cc = c - r * CR;
-        const int64_t m = m_beg + r;
-        v[i] = ld16(arow(p, shards, m) + k_beg + cc * 8);
-        dst[i] = m * p.K + k_beg + cc * 8;
+        v[i] = ld16(arow(p, shards, m_beg + r) + k_beg + cc * 8);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kFetchDepth; ++i) {
       const int c = base + i * kThreads + tid;
-      if (c < total) st16(p.staging + dst[i], v[i]);
+      if (c < total) {
+        const int r = c / CR, cc = c - r * CR;
+        st16(p.staging + (m_beg + r) * p.K + k_beg + cc * 8, v[i]);
+      }
     }
   }
 }
 
-// Copy unit (t_m, g) into m_contiguous staging: each thread transposes 8x8 blocks. Lanes
-// are ordered so that 8 lanes read 128 contiguous bytes of one row and 8 lanes write 128
-// contiguous bytes of one staging row.
+// Copy unit (t_m, g) into m_contiguous staging: each thread transposes 8x8 blocks, four at
+// a time. Lanes are ordered so that 8 lanes read 128 contiguous bytes of one row and 8
+// lanes write 128 contiguous bytes of one staging row.
 template <int BM>
 __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid) {
+  constexpr int NB = kFetchDepth / 8;  // blocks per thread in flight
   const int64_t m_beg = (int64_t)t_m * BM;
   const int R = (int)min((int64_t)BM, p.M - m_beg);       // multiple of 8
   const int64_t k_beg = (int64_t)g * KG;
   const int NBK = (int)(min((int64_t)KG, p.K - k_beg) / 8);
   const int NBM = R / 8;
   const int total = ((NBK + 7) & ~7) * NBM;
-  for (int b = tid; b < total; b += kThreads) {
-    const int kb = (b / (8 * NBM)) * 8 + (b & 7);
-    const int mb = (b >> 3) % NBM;
-    if (kb >= NBK) continue;
-    u32x4 v[8];
+  for (int b0 = tid; b0 < total; b0 += kThreads * NB) {
+    u32x4 v[NB][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ld16(arow(p, shards, m_beg + mb * 8 + j) + k_beg + kb * 8);
-    uint16_t* dst = p.staging + (k_beg + kb * 8) * p.M + m_beg + mb * 8;
+    for (int q = 0; q < NB; ++q) {
+      const int b = b0 + q * kThreads;
+      const int kb = (b / (8 * NBM)) * 8 + (b & 7);
+      const int mb = (b >> 3) % NBM;
+      if (b < total && kb < NBK) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st16(dst + (int64_t)i * p.M, transpose_row(v, i));
+        for (int j = 0; j < 8; ++j)
+          v[q][j] = ld16(arow(p, shards, m_beg + mb * 8 + j) + k_beg + kb * 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int b = b0 + q * kThreads;
+      const int kb = (b / (8 * NBM)) * 8 + (b & 7);
+      const int mb = (b >> 3) % NBM;
+      if (b < total && kb < NBK) {
+        uint16_t* dst = p.staging + (k_beg + kb * 8) * p.M + m_beg + mb * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st16(dst + (int64_t)i * p.M, transpose_row(v[q], i));
+      }
+    }
   }
 }
 
 // Units f, f+F, f+2F, ... of the fetch order. publish: fused mode, set each unit's flag.
-template <class T>
+template <class T, bool LAYOUT_K>
 __device__ void fetch_loop(const KParams& p, const uint16_t* const* shards, int f, int F,
                            bool publish, Tracer& tr, int tid) {
   const int KG = p.kpf * T::BK;
   for (int u = f; u < p.num_units; u += F) {
     const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
     const uint64_t t0 = tr.now();
-    if (p.staged_kmajor)
+    if (LAYOUT_K)
       copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid);
     else
       copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid);
@@ -739,7 +758,9 @@ __device__ inline int grab(const KParams& p) {
   return -1;
 }
 
-template <int BM, int DT, bool FUSED>
+// FUSED: fetchers + flag waits; LAYOUT_K: staging is k_contiguous (staged and in-place
+// tiles then share one K-major tile routine), else m_contiguous.
+template <int BM, int DT, bool FUSED, bool LAYOUT_K>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
   __shared__ u32x4 lds0[T::STAGE], lds1[T::STAGE], lds2[T::STAGE], lds3[T::STAGE];
@@ -761,7 +782,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
 
   if (FUSED && wg < p.F) {
     load_shard_table(p, s_shards, tid);
-    fetch_loop<T>(p, s_shards, wg, p.F, true, tr, tid);
+    fetch_loop<T, LAYOUT_K>(p, s_shards, wg, p.F, true, tr, tid);
   }
 
   if (tid == 0) s_next = grab(p);
@@ -776,8 +797,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
       gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
+    } else if constexpr (LAYOUT_K) {
+      gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
     } else {
-      if (!staged || p.staged_kmajor)
+      if (!staged)
         gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
       else
         gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
@@ -805,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void agmm_copy(KParams p) {
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   Tracer tr{nullptr, 0u, 0u, false};
   load_shard_table(p, s_shards, threadIdx.x);
-  fetch_loop<Tile<BM>>(p, s_shards, blockIdx.x, gridDim.x, false, tr, threadIdx.x);
+  fetch_loop<Tile<BM>, true>(p, s_shards, blockIdx.x, gridDim.x, false, tr, threadIdx.x);
 }
 
 __global__ void fill16_kernel(uint16_t* dst, int64_t n, uint16_t v) {
@@ -820,31 +843,49 @@ __global__ void fill32_kernel(uint32_t* dst, int64_t n, uint32_t v) {
     dst[i] = v;
 }
 
-template <int BM, int DT, bool FUSED>
+template <int BM, int DT, bool FUSED, bool LAYOUT_K>
 hipError_t launch_t(const KParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((agmm_persistent<BM, DT, FUSED>), dim3(grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((agmm_persistent<BM, DT, FUSED, LAYOUT_K>), dim3(grid), dim3(kThreads), 0, s,
+                     p);
   return hipGetLastError();
 }
 
+template <int BM, bool FUSED, bool LAYOUT_K>
+hipError_t launch_dt(const KParams& p, int dtype, int grid, hipStream_t s) {
+  return dtype == AGMM_BF16 ? launch_t<BM, AGMM_BF16, FUSED, LAYOUT_K>(p, grid, s)
+                            : launch_t<BM, AGMM_F16, FUSED, LAYOUT_K>(p, grid, s);
+}
+
+// The gemm-only kernel reads k_contiguous staging only.
 template <bool FUSED>
 hipError_t launch_any(const KParams& p, int dtype, int block_m, int grid, hipStream_t s) {
-  const bool bf = dtype == AGMM_BF16;
+  const bool lk = !FUSED || p.staged_kmajor;
   switch (block_m) {
     case 256:
-      return bf ? launch_t<256, AGMM_BF16, FUSED>(p, grid, s) : launch_t<256, AGMM_F16, FUSED>(p, grid, s);
+      return lk ? launch_dt<256, FUSED, true>(p, dtype, grid, s)
+                : launch_dt<256, FUSED, !FUSED>(p, dtype, grid, s);
     case 128:
-      return bf ? launch_t<128, AGMM_BF16, FUSED>(p, grid, s) : launch_t<128, AGMM_F16, FUSED>(p, grid, s);
+      return lk ? launch_dt<128, FUSED, true>(p, dtype, grid, s)
+                : launch_dt<128, FUSED, !FUSED>(p, dtype, grid, s);
     case 64:
-      return bf ? launch_t<64, AGMM_BF16, FUSED>(p, grid, s) : launch_t<64, AGMM_F16, FUSED>(p, grid, s);
+      return lk ? launch_dt<64, FUSED, true>(p, dtype, grid, s)
+                : launch_dt<64, FUSED, !FUSED>(p, dtype, grid, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
+// The occupancy of the heavier of the two fused variants.
 template <int BM, int DT>
 hipError_t occ_t(int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      per_cu, reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true>), kThreads, 0);
+  int a = 0, b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &a, reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, true>), kThreads, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b, reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, false>), kThreads, 0);
+  *per_cu = a < b ? a : b;
+  return e;
 }
 
 }  // namespace
