@@ -648,7 +648,34 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
 // workgroup's copy rate is bound by latency, not by its share of the HBM bandwidth.
 constexpr int kFetchDepth = 32;
 
-// Copy unit (t_m, g) into k_contiguous staging: 16-byte loads, then 16-byte stores.
+// Source row pointers of one unit: rows m_beg .. m_beg + R - 1 of the gathered A. A unit
+// inside one shard (the usual case) needs no per-row shard lookup.
+struct UnitRows {
+  const uint16_t* base;  // row m_beg when the unit lies in one shard, else nullptr
+  __device__ inline UnitRows(const KParams& p, const uint16_t* const* shards, int64_t m_beg,
+                             int R) {
+    const int64_t d0 = m_beg / p.M_s, d1 = (m_beg + R - 1) / p.M_s;
+    base = d0 == d1 ? shards[d0] + (m_beg - d0 * p.M_s) * p.K : nullptr;
+  }
+  __device__ inline const uint16_t* row(const KParams& p, const uint16_t* const* shards,
+                                        int64_t m_beg, int r) const {
+    return base ? base + (int64_t)r * p.K : arow(p, shards, m_beg + r);
+  }
+};
+
+__device__ inline u32x4 bload16(rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+__device__ inline void bstore16(rsrc_t rs, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rs, (int)off, 0, 0);
+}
+
+// Copy unit (t_m, g) into k_contiguous staging: 16-byte loads, then 16-byte stores. Chunk
+// c = r * CR + cc of the unit goes to thread c % 256; the (r, cc) of successive chunks of a
+// thread advance by fixed steps, so the loop does no division. When the unit lies in one
+// shard (the usual case) the loads and stores are range-checked buffer accesses: a lane
+// past the unit reads zero and its store is dropped, so the loop has no branch and all
+// kFetchDepth loads stay in flight.
 template <int BM>
 __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid) {
@@ -656,31 +683,51 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
   const int R = (int)min((int64_t)BM, p.M - m_beg);
   const int64_t k_beg = (int64_t)g * KG;
   const int CR = (int)(min((int64_t)KG, p.K - k_beg) / 8);
-  const int total = R * CR;
-  for (int base = 0; base < total; base += kThreads * kFetchDepth) {
-    u32x4 v[kFetchDepth];
+  if (CR <= 0 || R <= 0) return;
+  const UnitRows rows(p, shards, m_beg, R);
+  const int dr = kThreads / CR, dc = kThreads - dr * CR;  // step of (r, cc) per chunk
+  int r = tid / CR, cc = tid - (tid / CR) * CR;
+  const int64_t span = (int64_t)R * p.K * 2;  // bytes of the unit's row range
+  if (rows.base && span <= 0x7fffffffll) {
+    const rsrc_t src = make_rsrc(rows.base, span);
+    const rsrc_t dst = make_rsrc(p.staging + m_beg * p.K, span);
+    while (r < R) {
+      u32x4 v[kFetchDepth];
+      uint32_t off[kFetchDepth];
 #pragma unroll
-    for (int i = 0; i < kFetchDepth; ++i) {
-      const int c = base + i * kThreads + tid;
-      if (c < total) {
-        const int r = c / CR, cc = c - r * CR;
-        v[i] = ld16(arow(p, shards, m_beg + r) + k_beg + cc * 8);
+      for (int i = 0; i < kFetchDepth; ++i) {
+        off[i] = r < R ? (uint32_t)(((int64_t)r * p.K + k_beg + cc * 8) * 2) : kOob;
+        v[i] = bload16(src, off[i]);
+        r += dr;
+        cc += dc;
+        if (cc >= CR) {
+          cc -= CR;
+          ++r;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < kFetchDepth; ++i) bstore16(dst, off[i], v[i]);
     }
-#pragma unroll
-    for (int i = 0; i < kFetchDepth; ++i) {
-      const int c = base + i * kThreads + tid;
-      if (c < total) {
-        const int r = c / CR, cc = c - r * CR;
-        st16(p.staging + (m_beg + r) * p.K + k_beg + cc * 8, v[i]);
-      }
+    return;
+  }
+  uint16_t* const dst0 = p.staging + m_beg * p.K + k_beg;
+  for (; r < R;) {
+    const u32x4 v = ld16(rows.row(p, shards, m_beg, r) + k_beg + cc * 8);
+    st16(dst0 + (int64_t)r * p.K + cc * 8, v);
+    r += dr;
+    cc += dc;
+    if (cc >= CR) {
+      cc -= CR;
+      ++r;
     }
   }
 }
 
-// Copy unit (t_m, g) into m_contiguous staging: each thread transposes 8x8 blocks, four at
-// a time. Lanes are ordered so that 8 lanes read 128 contiguous bytes of one row and 8
-// lanes write 128 contiguous bytes of one staging row.
+// Copy unit (t_m, g) into m_contiguous staging: each thread transposes 8x8 blocks (8 rows x
+// 8 K values), four at a time. Block (kb, mb) is numbered b with kb = (b / (8 NBM)) * 8 +
+// b % 8 and mb = (b / 8) % NBM, so 8 consecutive lanes read 128 contiguous bytes of one row;
+// a thread's blocks b, b + 256, ... advance (kb, mb) by fixed steps (no division). Same
+// buffer-access fast path as the k_contiguous copy.
 template <int BM>
 __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid) {
@@ -690,30 +737,60 @@ __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards
   const int64_t k_beg = (int64_t)g * KG;
   const int NBK = (int)(min((int64_t)KG, p.K - k_beg) / 8);
   const int NBM = R / 8;
-  const int total = ((NBK + 7) & ~7) * NBM;
-  for (int b0 = tid; b0 < total; b0 += kThreads * NB) {
-    u32x4 v[NB][8];
+  if (NBK <= 0 || NBM <= 0) return;
+  const UnitRows rows(p, shards, m_beg, R);
+  // t = b / 8 = kbh * NBM + mb; a thread's t advances by 32 per block
+  const int dkh = (kThreads / 8) / NBM, dmb = (kThreads / 8) - dkh * NBM;
+  const int t0 = tid >> 3, lo = tid & 7;
+  int kbh = t0 / NBM, mb = t0 - (t0 / NBM) * NBM;
+  const int64_t sspan = (int64_t)R * p.K * 2, dspan = (int64_t)NBK * 8 * p.M * 2;
+  if (rows.base && sspan <= 0x7fffffffll && dspan <= 0x7fffffffll) {
+    const rsrc_t src = make_rsrc(rows.base, sspan);
+    const rsrc_t dst = make_rsrc(p.staging + k_beg * p.M + m_beg, dspan - m_beg * 2);
+    while (kbh * 8 < NBK) {
+      u32x4 v[NB][8];
+      uint32_t doff[NB];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int b = b0 + q * kThreads;
-      const int kb = (b / (8 * NBM)) * 8 + (b & 7);
-      const int mb = (b >> 3) % NBM;
-      if (b < total && kb < NBK) {
+      for (int q = 0; q < NB; ++q) {
+        const int kb = kbh * 8 + lo;
+        const bool ok = kb < NBK;
+        const uint32_t soff = (uint32_t)((((int64_t)mb * 8) * p.K + k_beg + kb * 8) * 2);
+        doff[q] = ok ? (uint32_t)(((int64_t)kb * 8 * p.M + mb * 8) * 2) : kOob;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          v[q][j] = ld16(arow(p, shards, m_beg + mb * 8 + j) + k_beg + kb * 8);
+          v[q][j] = bload16(src, ok ? soff + (uint32_t)(j * p.K * 2) : kOob);
+        kbh += dkh;
+        mb += dmb;
+        if (mb >= NBM) {
+          mb -= NBM;
+          ++kbh;
+        }
       }
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          bstore16(dst, doff[q] == kOob ? kOob : doff[q] + (uint32_t)(i * p.M * 2),
+                   transpose_row(v[q], i));
     }
+    return;
+  }
+  while (kbh * 8 < NBK) {
+    const int kb = kbh * 8 + lo;
+    if (kb < NBK) {
+      u32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int b = b0 + q * kThreads;
-      const int kb = (b / (8 * NBM)) * 8 + (b & 7);
-      const int mb = (b >> 3) % NBM;
-      if (b < total && kb < NBK) {
-        uint16_t* dst = p.staging + (k_beg + kb * 8) * p.M + m_beg + mb * 8;
+      for (int j = 0; j < 8; ++j)
+        v[j] = ld16(rows.row(p, shards, m_beg, mb * 8 + j) + k_beg + kb * 8);
+      uint16_t* dst = p.staging + (k_beg + kb * 8) * p.M + m_beg + mb * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st16(dst + (int64_t)i * p.M, transpose_row(v[q], i));
-      }
+      for (int i = 0; i < 8; ++i) st16(dst + (int64_t)i * p.M, transpose_row(v, i));
+    }
+    kbh += dkh;
+    mb += dmb;
+    if (mb >= NBM) {
+      mb -= NBM;
+      ++kbh;
     }
   }
 }
