@@ -29,7 +29,8 @@ ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "OOM", -5: "TIMEO
 F16, BF16 = 0, 1
 K_CONTIGUOUS, M_CONTIGUOUS = 0, 1
 ALGO_FUSED, ALGO_BASELINE = 0, 1
-Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES, Q_QUEUES = range(1, 9)
+Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES, Q_QUEUES, Q_PARTIALS = \
+    range(1, 10)
 EV_FETCH, EV_GEMM, EV_GEMM_WAIT = 1, 2, 3
 
 EXPORTED = [
@@ -48,7 +49,8 @@ class agmm_desc(ctypes.Structure):
         ("block_m", ctypes.c_int32), ("k_per_flag", ctypes.c_int32),
         ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
-        ("debug_skip_unit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+        ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -61,7 +63,9 @@ class agmm_config(ctypes.Structure):
         ("num_copy_wgs", ctypes.c_int32), ("trace_cap", ctypes.c_int32),
         ("epoch", ctypes.c_uint32), ("staging_elems", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
-        ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
+        ("num_cus", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
+        ("split_pieces", ctypes.c_int32), ("num_items", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
     def as_dict(self):
@@ -252,11 +256,20 @@ class AgMatmul:
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_MTILES, n * 4), dtype="<u4")
 
     def queues(self):
-        """[(queue tile ids)] for the 8 per-XCD tile queues."""
-        n = self.config.num_tiles
-        raw = np.frombuffer(ag_matmul_debug_query(self.handle, Q_QUEUES, (16 + n) * 4), dtype="<u4")
-        off, ln, tiles = raw[:8], raw[8:16], raw[16:]
-        return [list(map(int, tiles[o:o + l])) for o, l in zip(off, ln)]
+        """The 9 queues (8 per-XCD, then the tail queue of split-tile pieces) as lists of
+        entries: tile id | piece << 24 | (pieces - 1) << 28."""
+        n = self.config.num_items
+        raw = np.frombuffer(ag_matmul_debug_query(self.handle, Q_QUEUES, (18 + n) * 4), dtype="<u4")
+        off, ln, ents = raw[:9], raw[9:18], raw[18:]
+        return [list(map(int, ents[o:o + l])) for o, l in zip(off, ln)]
+
+    def partials(self) -> np.ndarray:
+        """fp32 partial sums of the split tiles, [split tile][piece][block_m * block_n] in the
+        slot layout of AGMM_Q_PARTIALS."""
+        c = self.config
+        n = c.split_tiles * c.split_pieces * c.block_m * c.block_n
+        raw = np.frombuffer(ag_matmul_debug_query(self.handle, Q_PARTIALS, n * 4), dtype="<f4")
+        return raw.reshape(c.split_tiles, max(1, c.split_pieces), c.block_m * c.block_n)
 
     def status(self) -> np.ndarray:
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STATUS, 16), dtype="<u4")

@@ -24,10 +24,13 @@ struct agmm_handle {
   agmm_trace_rec* trace;
   uint32_t* trace_count;
   int64_t flags_n;
+  int64_t split_base;
   int64_t trace_wgs;        // workgroups the trace buffer has room for
   uint32_t* qtiles;
+  uint32_t* split_cnt;
+  float* partials;
   std::vector<uint32_t> h_units, h_mtiles, h_qtiles;
-  int32_t qoff[agmm::kQueues], qlen[agmm::kQueues];
+  int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
   bool poisoned;
 };
 
@@ -71,6 +74,7 @@ int validate_desc(const agmm_desc* d) {
   if (d->k_per_flag < 0 || d->num_fetch_wgs < 0 || d->num_wgs < 0 || d->trace_cap < 0)
     return AGMM_ERR_INVALID_ARG;
   if (d->debug_skip_unit < -1) return AGMM_ERR_INVALID_ARG;
+  if (d->tail_split != 0 && d->tail_split != 1) return AGMM_ERR_INVALID_ARG;
   if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
   if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
     return AGMM_ERR_UNSUPPORTED;
@@ -88,10 +92,10 @@ struct Plan {
   agmm_config cfg;
   int64_t M_s;
   std::vector<uint32_t> units, mtiles, qtiles;
-  int32_t qoff[agmm::kQueues], qlen[agmm::kQueues];
-  int64_t flags_n, trace_wgs;
-  int64_t off_staging, off_flags, off_ctr, off_units, off_mtiles, off_qtiles, off_trace,
-      off_tcount, total;
+  int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
+  int64_t flags_n, trace_wgs, split_base;
+  int64_t off_staging, off_flags, off_ctr, off_split, off_units, off_mtiles, off_qtiles,
+      off_partials, off_trace, off_tcount, total;
 };
 
 // Tile queues (one per XCD): GEMM-order m-tiles are taken in super-rows of kSuperRows; a
@@ -101,18 +105,32 @@ struct Plan {
 constexpr int kSuperRows = 4;
 constexpr int kColBlock = 8;
 
-void make_queues(int64_t T_m, int64_t T_n, Plan* pl) {
-  std::vector<std::vector<uint32_t>> qs(agmm::kQueues);
+// Split tiles (tiles t_m * T_n + t_n >= split_base, when S >= 2) stay out of the XCD queues;
+// their pieces, S per tile in tile order, form the tail queue.
+void make_queues(int64_t T_m, int64_t T_n, const std::vector<uint32_t>& mtiles, int S,
+                 Plan* pl) {
+  std::vector<std::vector<uint32_t>> qs(agmm::kQueueSlots);
+  std::vector<int64_t> pos_of(T_m);
+  for (int64_t pos = 0; pos < T_m; ++pos) pos_of[mtiles[pos] & 0x7fffffffu] = pos;
+  auto split = [&](int64_t pos, int64_t n) {
+    return S >= 2 && (int64_t)(mtiles[pos] & 0x7fffffffu) * T_n + n >= pl->split_base;
+  };
   for (int64_t s0 = 0, j = 0; s0 < T_m; s0 += kSuperRows, ++j) {
     const int64_t s1 = std::min(T_m, s0 + kSuperRows);
     auto& q = qs[j % agmm::kQueues];
     for (int64_t nb = 0; nb < T_n; nb += kColBlock)
       for (int64_t pos = s0; pos < s1; ++pos)
         for (int64_t n = nb; n < std::min(T_n, nb + kColBlock); ++n)
-          q.push_back((uint32_t)(pos * T_n + n));
+          if (!split(pos, n)) q.push_back((uint32_t)(pos * T_n + n));
   }
+  if (S >= 2)
+    for (int64_t c = pl->split_base; c < T_m * T_n; ++c) {
+      const uint32_t q = (uint32_t)(pos_of[c / T_n] * T_n + c % T_n);
+      for (int piece = 0; piece < S; ++piece)
+        qs[agmm::kTailQueue].push_back(q | ((uint32_t)piece << 24) | ((uint32_t)(S - 1) << 28));
+    }
   pl->qtiles.clear();
-  for (int x = 0; x < agmm::kQueues; ++x) {
+  for (int x = 0; x < agmm::kQueueSlots; ++x) {
     pl->qoff[x] = (int32_t)pl->qtiles.size();
     pl->qlen[x] = (int32_t)qs[x].size();
     pl->qtiles.insert(pl->qtiles.end(), qs[x].begin(), qs[x].end());
@@ -166,13 +184,33 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   if (n_units >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
   c.num_units = (int32_t)n_units;
 
+  // Tail split: with Wg GEMM workgroups, num_tiles % Wg tiles are left for a last round. When
+  // that round would be at most half full, the last tiles (by t_m * T_n + t_n) are cut along
+  // K into S pieces (at least 16 K-tiles each) so the round has about Wg pieces.
+  const int64_t W_base = std::min<int64_t>(d.num_wgs ? d.num_wgs : num_cus, num_cus);
+  const int64_t Wg = std::min<int64_t>(W_base, c.num_tiles);
+  const int64_t KT = cdiv(d.K, c.block_k);
+  int S = 0;
+  int64_t tail = 0;
+  if (d.tail_split == 1 && Wg > 0 && c.num_tiles > Wg && c.num_tiles <= (int64_t)agmm::kItemTileMask) {
+    tail = c.num_tiles % Wg;
+    if (tail > 0) {
+      S = (int)std::min<int64_t>({(int64_t)agmm::kMaxSplit, Wg / tail, KT / 16});
+      if (S < 2) S = 0;
+    }
+    if (S == 0) tail = 0;
+  }
+  c.split_tiles = (int32_t)tail;
+  c.split_pieces = S;
+  c.num_items = (int32_t)(c.num_tiles + tail * (S > 0 ? S - 1 : 0));
+  pl->split_base = c.num_tiles - tail;
+
   // Grid: one workgroup per CU (a 128 KiB LDS footprint allows one), fetchers first.
   int F = 0;
   if (n_units > 0) F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
   F = (int)std::min<int64_t>(F, n_units);
-  int64_t W = d.num_wgs ? d.num_wgs : num_cus;
-  W = std::min<int64_t>(W, num_cus);                  // every workgroup resident
-  W = std::min<int64_t>(W, (int64_t)F + c.num_tiles);  // no idle workgroups
+  int64_t W = W_base;                                  // every workgroup resident
+  W = std::min<int64_t>(W, (int64_t)F + c.num_items);  // no idle workgroups
   F = (int)std::min<int64_t>(F, W);
   if (c.num_tiles > 0 && W < 1) W = 1;
   c.num_fetch_wgs = F;
@@ -192,7 +230,7 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
       }
   }
 
-  make_queues(T_m, T_n, pl);
+  make_queues(T_m, T_n, pl->mtiles, S, pl);
 
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
   pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
@@ -203,9 +241,11 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   pl->off_staging = off; off = align256(off + c.staging_elems * 2);
   pl->off_flags = off;   off = align256(off + pl->flags_n * 4);
   pl->off_ctr = off;     off = align256(off + agmm::CTR_WORDS * 4);
+  pl->off_split = off;   off = align256(off + std::max<int64_t>(1, tail) * 4);
   pl->off_units = off;   off = align256(off + std::max<int64_t>(1, n_units) * 8);
   pl->off_mtiles = off;  off = align256(off + std::max<int64_t>(1, T_m) * 4);
-  pl->off_qtiles = off;  off = align256(off + std::max<int64_t>(1, T_m * T_n) * 4);
+  pl->off_qtiles = off;  off = align256(off + std::max<int64_t>(1, c.num_items) * 4);
+  pl->off_partials = off; off = align256(off + tail * S * (int64_t)bm * bm * 4);
   pl->off_trace = off;   off = align256(off + pl->trace_wgs * c.trace_cap * (int64_t)sizeof(agmm_trace_rec));
   pl->off_tcount = off;  off = align256(off + std::max<int64_t>(1, pl->trace_wgs) * 4);
   pl->total = off;
@@ -305,6 +345,9 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   h->units = reinterpret_cast<uint32_t*>(h->ws + pl.off_units);
   h->mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_mtiles);
   h->qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_qtiles);
+  h->split_cnt = reinterpret_cast<uint32_t*>(h->ws + pl.off_split);
+  h->partials = reinterpret_cast<float*>(h->ws + pl.off_partials);
+  h->split_base = pl.split_base;
   h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
   h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
 
@@ -314,7 +357,8 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
     delete h;
     return AGMM_ERR_HIP;
   };
-  // Flags, counters and trace counts start at zero; the schedule tables are uploaded once.
+  // Flags, counters (queues, split tiles) and trace counts start at zero; the schedule
+  // tables are uploaded once.
   if ((e = hipMemset(h->ws + pl.off_flags, 0, (size_t)(pl.off_units - pl.off_flags))) != hipSuccess)
     return fail(e);
   if (pl.trace_wgs &&
@@ -389,6 +433,7 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
     AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
+    AGMM_HIP(agmm::launch_fill32(h->split_cnt, c.split_tiles, 0u, s));
     h->cfg.epoch = 0;
   }
   const uint32_t epoch = ++h->cfg.epoch;
@@ -405,10 +450,13 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   p.units = h->units;
   p.mtiles = h->mtiles;
   p.qtiles = h->qtiles;
-  for (int x = 0; x < agmm::kQueues; ++x) {
+  for (int x = 0; x < agmm::kQueueSlots; ++x) {
     p.qoff[x] = h->qoff[x];
     p.qlen[x] = h->qlen[x];
   }
+  p.partials = h->partials;
+  p.split_cnt = h->split_cnt;
+  p.split_base = (int32_t)h->split_base;
   p.trace = h->trace;
   p.trace_count = h->trace_count;
   p.M = d.M;
@@ -439,7 +487,8 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
     p.debug = 0;
     p.trace_cap = 0;
     if (c.num_units > 0) AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
-    const int grid = std::min(c.num_cus, c.num_tiles);
+    const int grid = (int)std::min<int64_t>(std::min(c.num_cus, c.num_items),
+                                            d.num_wgs ? d.num_wgs : c.num_cus);
     AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
   }
 
@@ -467,6 +516,10 @@ int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
     case AGMM_Q_TRACE: src = h->trace; n = (size_t)h->trace_wgs * c.trace_cap * sizeof(agmm_trace_rec); break;
     case AGMM_Q_TRACE_COUNT: src = h->trace_count; n = (size_t)h->trace_wgs * 4; break;
     case AGMM_Q_STATUS: src = h->ctr + agmm::CTR_STATUS; n = 16; break;
+    case AGMM_Q_PARTIALS:
+      src = h->partials;
+      n = (size_t)c.split_tiles * c.split_pieces * c.block_m * c.block_n * 4;
+      break;
     case AGMM_Q_UNITS:
       if (bytes != h->h_units.size() * 4) return AGMM_ERR_INVALID_ARG;
       if (bytes) memcpy(dst, h->h_units.data(), bytes);
@@ -476,14 +529,15 @@ int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
       if (bytes) memcpy(dst, h->h_mtiles.data(), bytes);
       return AGMM_OK;
     case AGMM_Q_QUEUES: {
-      const size_t n = (2 * agmm::kQueues + h->h_qtiles.size()) * 4;
+      const size_t n = (2 * agmm::kQueueSlots + h->h_qtiles.size()) * 4;
       if (bytes != n) return AGMM_ERR_INVALID_ARG;
       uint32_t* o = static_cast<uint32_t*>(dst);
-      for (int x = 0; x < agmm::kQueues; ++x) {
+      for (int x = 0; x < agmm::kQueueSlots; ++x) {
         o[x] = (uint32_t)h->qoff[x];
-        o[agmm::kQueues + x] = (uint32_t)h->qlen[x];
+        o[agmm::kQueueSlots + x] = (uint32_t)h->qlen[x];
       }
-      if (!h->h_qtiles.empty()) memcpy(o + 2 * agmm::kQueues, h->h_qtiles.data(), h->h_qtiles.size() * 4);
+      if (!h->h_qtiles.empty())
+        memcpy(o + 2 * agmm::kQueueSlots, h->h_qtiles.data(), h->h_qtiles.size() * 4);
       return AGMM_OK;
     }
     default: return AGMM_ERR_INVALID_ARG;

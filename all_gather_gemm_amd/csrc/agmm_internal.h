@@ -15,6 +15,15 @@ constexpr int kBlockK = 32;    // K-tile depth of the GEMM worker (every tile fa
 // XCD w % 8 by the dispatcher); a workgroup drains its own queue, then steals from the
 // others.
 constexpr int kQueues = 8;
+// A ninth queue, taken from only when the XCD queues are empty, holds the pieces of the
+// tiles split along K to fill the last round (the tail); its index is kTailQueue.
+constexpr int kTailQueue = kQueues;
+constexpr int kQueueSlots = kQueues + 1;
+
+// Queue entry: bits 0-23 tile id (position of its m-tile in GEMM order * T_n + n-tile),
+// bits 24-27 piece, bits 28-31 pieces - 1 (0: the tile is not split).
+constexpr uint32_t kItemTileMask = 0x00ffffffu;
+constexpr int kMaxSplit = 4;
 
 // Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
 enum : int {
@@ -25,7 +34,7 @@ enum : int {
   CTR_STATUS_SEEN = 5,  // flag value it last saw
   CTR_Q = 32,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
   CTR_QSTRIDE = 32,
-  CTR_WORDS = CTR_Q + kQueues * CTR_QSTRIDE
+  CTR_WORDS = CTR_Q + kQueueSlots * CTR_QSTRIDE
 };
 
 // Everything a launch needs, passed by value as the kernel argument.
@@ -39,8 +48,11 @@ struct KParams {
   uint32_t* ctr;            // [CTR_WORDS]
   const uint32_t* units;    // [2 * num_units]: (m-tile, k-group) in fetch order
   const uint32_t* mtiles;   // [T_m]: m-tile in GEMM order; bit 31 set = read in place
-  const uint32_t* qtiles;   // [num_tiles]: tile ids, queue by queue
-  int32_t qoff[kQueues], qlen[kQueues];
+  const uint32_t* qtiles;   // [num_items]: queue entries, queue by queue
+  int32_t qoff[kQueueSlots], qlen[kQueueSlots];
+  float* partials;          // split tiles: [split tile][piece][BM*BN] fp32 partial sums
+  uint32_t* split_cnt;      // [split tiles]: pieces finished, S per run (epoch-valued)
+  int32_t split_base;       // tile (t_m * T_n + t_n) of the first split tile
   agmm_trace_rec* trace;    // [gridDim.x * trace_cap] (debug)
   uint32_t* trace_count;    // [gridDim.x] (debug)
   int64_t M, N, K, M_s;

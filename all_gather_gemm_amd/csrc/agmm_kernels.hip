@@ -34,6 +34,7 @@ namespace {
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -131,6 +132,15 @@ __device__ inline rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
                                            (int)uniform32((uint32_t)n), 0x00020000);
 }
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource range used here
+
+// 16-byte buffer load / store; out-of-range offsets read zero / write nothing.
+__device__ inline u32x4 bload16(rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+__device__ inline void bstore16(rsrc_t rs, uint32_t off, u32x4 v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rs, (int)off, 0, 0);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -283,6 +293,10 @@ __device__ inline void mfmas(f32x16 (&acc)[T::FM][T::FN], const u32x4 (&a)[T::FM
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = Num<DT>::mfma(b[fn], a[fm], acc[fm][fn]);
 }
 
+// 24 wait states: covers the longest MFMA result latency before an accumulator is read
+// by the inline-asm reads below (whose AGPR operands the hazard checks may not track).
+__device__ inline void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // One accumulator element, copied out of its AGPR where it is used. Left to itself the
 // register allocator moves every accumulator into VGPRs at the end of the K loop, which
 // does not fit and spills.
@@ -343,9 +357,16 @@ __device__ inline int grab(const KParams& p);
 // is done, so the queue atomic's round trip overlaps the epilogue while no tile is claimed
 // long before it can start (claiming at the start of a tile lets the first workgroups to
 // arrive take two tiles each and starve the rest when tiles and workgroups are few).
+// piece / pieces: a split tile's piece covers K-tiles [piece * KT / pieces, (piece + 1) * KT /
+// pieces); its fp32 partial sums go to a workspace slot and the piece that finishes the tile
+// last adds all of them in piece order (so the sum does not depend on which piece ends
+// last) and runs the epilogue. is_last: an LDS word for that decision.
 template <class T, int DT, bool A_KMAJOR, bool WAIT>
-__device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n, bool staged, const Stages<T>& st,
-                          u32x2* bias_lds, int tid, Tracer& tr, int* next_tile) {
+__device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n,
+                                                         int piece, int pieces, bool staged,
+                                                         const Stages<T>& st, u32x2* bias_lds,
+                                                         int tid, Tracer& tr, int* next_tile,
+                                                         int* is_last) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN;
@@ -371,8 +392,16 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   // step of the A base per K-tile: BK columns (K-major) or BK rows (m_contiguous)
   const int64_t a_step = A_KMAJOR ? (int64_t)BK : (int64_t)BK * lda;
   const uint16_t* bbase = p.B + n0;
-  const int64_t b_bytes = (p.K * p.N - n0) * 2;
+  int64_t b_bytes = (p.K * p.N - n0) * 2;
   const int64_t b_step = (int64_t)BK * p.N;
+  // this piece's K-tiles [kt_lo, kt_lo + KT): the operand bases start at kt_lo
+  const int KT_all = (int)((p.K + BK - 1) / BK);
+  const int kt_lo = piece * KT_all / pieces;
+  const int KT = (piece + 1) * KT_all / pieces - kt_lo;
+  abase += kt_lo * a_step;
+  a_bytes -= kt_lo * a_step * 2;
+  bbase += kt_lo * b_step;
+  b_bytes -= kt_lo * b_step * 2;
 
   using ADma = typename std::conditional<A_KMAJOR, KMajorDma<BM>, MNMajorDma<BM>>::type;
   using BDma = MNMajorDma<BN>;
@@ -395,7 +424,6 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
 
-  const int KT = (int)((p.K + BK - 1) / BK);
   const int64_t fbase = (int64_t)t_m * p.G;
   bool waits = WAIT && staged;
   const int kpf = p.kpf;
@@ -405,7 +433,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   // one acquire covers the whole tile and the K loop polls nothing.
   if (waits) {
     bool all = true;
-    for (int g = 0; g < p.G && all; ++g)
+    for (int g = kt_lo / kpf; g * kpf < kt_lo + KT && all; ++g)
       all = uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT)) == p.epoch;
     if (all) {
@@ -428,17 +456,18 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     rsrc_t ra, rb;
     int64_t k_rem;
   };
-  // Fused mode: wait for every staged k-group whose first K-tile lies in [lo, hi]. Called
-  // once per block of four K-tiles, before the block that requests them, so the polling
-  // code stays outside the unrolled MFMA stream.
+  // Fused mode: wait for every staged k-group whose first K-tile lies in [lo, hi] (K-tiles
+  // of this piece). Called once per block of four K-tiles, before the block that requests
+  // them, so the polling code stays outside the unrolled MFMA stream.
   auto wait_range = [&](int lo, int hi) {
     if (!waits) return;
-    for (int g = (lo + kpf - 1) / kpf; g * kpf <= hi; ++g) wait_flag(p, fbase + g, tr);
+    for (int g = (kt_lo + lo + kpf - 1) / kpf; g * kpf <= kt_lo + hi; ++g)
+      wait_flag(p, fbase + g, tr);
   };
   auto resources = [&](int t) -> Req {
     const int64_t ka = t * a_step, kb = t * b_step;
     return Req{make_rsrc(abase + ka, a_bytes - ka * 2), make_rsrc(bbase + kb, b_bytes - kb * 2),
-               p.K - (int64_t)t * BK};
+               p.K - (int64_t)(kt_lo + t) * BK};
   };
   const uint32_t wave_u = uniform32((uint32_t)wave);
   auto issue = [&](int d, const Req& r, uint32_t stage_off) {
@@ -535,6 +564,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   using NO = std::false_type;
 
   if (KT > 0) {
+    if (waits && kt_lo % kpf != 0) wait_flag(p, fbase + kt_lo / kpf, tr);  // group begun earlier
     wait_range(0, min(KT - 1, 3));
     request(0, st.off[0]);
     if (KT > 1) request(1, st.off[1]);
@@ -579,6 +609,41 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   __builtin_amdgcn_sched_barrier(0);
   if (tid == 0) *next_tile = grab(p);
 
+  // Split tile: this piece's partial sums go to its slot (4-float group (fm, fn, g) of
+  // thread tid at index ((fm * FN + fn) * 4 + g) * kThreads + tid, so a wave writes 1 KiB
+  // runs), then the piece is counted; only the piece that completes the tile goes on.
+  bool finish_split = false;  // this piece completes a split tile
+  const u32x4* parts = nullptr;
+  mfma_drain();
+  if (pieces > 1) {
+    const int64_t sidx = (int64_t)t_m * p.T_n + t_n - p.split_base;
+    u32x4* slots = reinterpret_cast<u32x4*>(p.partials + sidx * pieces * (BM * BN));
+    u32x4* mine = slots + (int64_t)piece * (BM * BN / 4);
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          mine[((fm * T::FN + fn) * 4 + g) * kThreads + tid] =
+              u32x4{__builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 0)),
+                    __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 1)),
+                    __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 2)),
+                    __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 3))};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(p.split_cnt + sidx, 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT) + 1u;
+      *is_last = done == (uint32_t)pieces * p.epoch;  // counters grow by `pieces` per run
+    }
+    __syncthreads();
+    if (!*is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    parts = slots;
+    finish_split = true;
+  }
+
   // Epilogue through LDS (all stages are free: every DMA has landed and the last barrier
   // is behind every wave): each lane adds the bias in fp32, rounds once (RNE) and writes 4
   // consecutive outputs (8 bytes) of one row into the output tile, whose row quarter
@@ -594,29 +659,69 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   auto unit_ptr = [&](int r, int u) -> uint32_t* {
     return reinterpret_cast<uint32_t*>(st.s[r / QR]) + ((r % QR) * ROW_U + u) * 2;
   };
+  // The accumulators to LDS; SPLIT: plus the other pieces' partial sums, added in piece
+  // order (reads past the last piece are out of the slots' range and return zeros, so
+  // the code has no branch). Two copies, chosen once per tile.
+  auto to_lds = [&](auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    const rsrc_t prs = make_rsrc(reinterpret_cast<const uint16_t*>(parts),
+                                 SPLIT ? (int64_t)pieces * BM * BN * 4 : 0);
 #pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm) {
-    const int ml = wm * T::WTM + fm * 32 + (lane & 31);
+    for (int fm = 0; fm < T::FM; ++fm) {
+      const int ml = wm * T::WTM + fm * 32 + (lane & 31);
 #pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) {
+      for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * T::WTN + fn * 32 + g * 8 + (lane >> 5) * 4;
-        float x0 = acc_read(acc[fm][fn], 4 * g + 0), x1 = acc_read(acc[fm][fn], 4 * g + 1);
-        float x2 = acc_read(acc[fm][fn], 4 * g + 2), x3 = acc_read(acc[fm][fn], 4 * g + 3);
-        const u32x2 bb = bias_lds[nl >> 2];
-        x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
-        x1 += Num<DT>::from_bits(bb[0] >> 16);
-        x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
-        x3 += Num<DT>::from_bits(bb[1] >> 16);
-        u32x2 o;
-        o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
-        o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
-        *reinterpret_cast<u32x2*>(unit_ptr(ml, (nl >> 2) ^ (ml & XM))) = o;
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * T::WTN + fn * 32 + g * 8 + (lane >> 5) * 4;
+          float x0 = acc_read(acc[fm][fn], 4 * g + 0), x1 = acc_read(acc[fm][fn], 4 * g + 1);
+          float x2 = acc_read(acc[fm][fn], 4 * g + 2), x3 = acc_read(acc[fm][fn], 4 * g + 3);
+          if constexpr (SPLIT) {
+            const uint32_t e = (uint32_t)(((fm * T::FN + fn) * 4 + g) * kThreads + tid) * 16u;
+            float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+            // The loaded vectors pass through an empty asm that takes them whole: when only
+            // some lanes of a 16-byte buffer load are read, the optimizer narrows it to
+            // dword loads and reads the same dword for every element.
+            u32x4 lv[kMaxSplit];
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp)
+              lv[sp] = bload16(prs, (uint32_t)sp * (BM * BN * 4) + e);
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp) asm volatile("" : "+v"(lv[sp]));
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp) {
+              const f32x4 lf = __builtin_bit_cast(f32x4, lv[sp]);
+              const bool own = sp == piece;
+              const float v0 = own ? x0 : lf.x;
+              const float v1 = own ? x1 : lf.y;
+              const float v2 = own ? x2 : lf.z;
+              const float v3 = own ? x3 : lf.w;
+              if (sp == 0) {
+                y0 = v0, y1 = v1, y2 = v2, y3 = v3;
+              } else {
+                y0 += v0, y1 += v1, y2 += v2, y3 += v3;
+              }
+            }
+            x0 = y0, x1 = y1, x2 = y2, x3 = y3;
+          }
+          const u32x2 bb = bias_lds[nl >> 2];
+          x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
+          x1 += Num<DT>::from_bits(bb[0] >> 16);
+          x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
+          x3 += Num<DT>::from_bits(bb[1] >> 16);
+          u32x2 o;
+          o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
+          o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
+          *reinterpret_cast<u32x2*>(unit_ptr(ml, (nl >> 2) ^ (ml & XM))) = o;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  if (finish_split)
+    to_lds(std::true_type{});
+  else
+    to_lds(std::false_type{});
   __syncthreads();
   constexpr int ROW_C = BN / 8;  // 16-byte chunks per row
 #pragma unroll 4
@@ -663,12 +768,6 @@ struct UnitRows {
   }
 };
 
-__device__ inline u32x4 bload16(rsrc_t rs, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
-}
-__device__ inline void bstore16(rsrc_t rs, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rs, (int)off, 0, 0);
-}
 
 // Copy unit (t_m, g) into k_contiguous staging: 16-byte loads, then 16-byte stores. Chunk
 // c = r * CR + cc of the unit goes to thread c % 256; the (r, cc) of successive chunks of a
@@ -818,12 +917,13 @@ __device__ void fetch_loop(const KParams& p, const uint16_t* const* shards, int 
   }
 }
 
-// Next tile for this workgroup, or -1: its XCD's queue first, then the other queues.
+// Next queue entry for this workgroup, or -1: its XCD's queue first, then the other XCD
+// queues, then the tail queue of split-tile pieces.
 __device__ inline int grab(const KParams& p) {
   if (aborted(p)) return -1;
   const int x0 = (int)(blockIdx.x % kQueues);
-  for (int s = 0; s < kQueues; ++s) {
-    const int x = (x0 + s) % kQueues;
+  for (int s = 0; s < kQueueSlots; ++s) {
+    const int x = s < kQueues ? (x0 + s) % kQueues : kTailQueue;
     uint32_t* c = p.ctr + CTR_Q + x * CTR_QSTRIDE;
     const uint32_t len = (uint32_t)p.qlen[x];
     if (len == 0) continue;
@@ -851,7 +951,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   st.off[1] = (uint32_t)(size_t)(lds_void*)lds1;
   st.off[2] = (uint32_t)(size_t)(lds_void*)lds2;
   st.off[3] = (uint32_t)(size_t)(lds_void*)lds3;
-  __shared__ int s_next;
+  __shared__ int s_next, s_last;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
   Tracer tr{p.debug ? p.trace + (size_t)wg * p.trace_cap : nullptr, 0u, (uint32_t)p.trace_cap,
@@ -867,20 +967,22 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   int q = __builtin_amdgcn_readfirstlane(s_next);  // uniform: tile addressing in SGPRs
   while (q >= 0) {
     __syncthreads();  // everyone has read s_next
-    const int pos = q / p.T_n, t_n = q - pos * p.T_n;
+    const int tile = (int)((uint32_t)q & kItemTileMask);
+    const int piece = ((uint32_t)q >> 24) & 15, pieces = (int)((uint32_t)q >> 28) + 1;
+    const int pos = tile / p.T_n, t_n = tile - pos * p.T_n;
     const uint32_t e = p.mtiles[pos];
     const int t_m = (int)(e & 0x7fffffffu);
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else if constexpr (LAYOUT_K) {
-      gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
+      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else {
       if (!staged)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, staged, st, s_bias, tid, tr, &s_next);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     __syncthreads();
@@ -891,7 +993,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     if (p.debug) p.trace_count[wg] = tr.n;
     const uint32_t old = atomicAdd(p.ctr + CTR_DONE, 1u);
     if (old == gridDim.x - 1) {  // last workgroup out resets the queues for the next run
-      for (int x = 0; x < kQueues; ++x)
+      for (int x = 0; x < kQueueSlots; ++x)
         __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

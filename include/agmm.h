@@ -82,7 +82,13 @@ typedef struct agmm_desc {
   int32_t trace_cap;     /* debug trace records per workgroup; 0 = auto */
   uint32_t spin_limit;   /* flag polls before a wait gives up; 0 = auto (several seconds) */
   int32_t debug_skip_unit; /* debug: fetch unit whose flag is never published; -1 = none */
-  int32_t reserved[3];
+  int32_t tail_split;    /* 1: when the tiles leave a last round at most half full, its
+                            tiles are split along K into pieces (fp32 partial sums, added
+                            in piece order by the piece that finishes last) so every
+                            workgroup has work; 0 (default): never split. Measured on the
+                            16384x3584x8192 workload the dynamic tile queues already even
+                            out most of that round and the split does not pay. */
+  int32_t reserved[2];
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
@@ -100,7 +106,10 @@ typedef struct agmm_config {
   int64_t workspace_bytes;      /* device bytes the handle owns */
   int32_t device;               /* HIP device the handle was created on */
   int32_t num_cus;
-  int32_t reserved[4];
+  int32_t split_tiles;          /* tail tiles split along K (the last ones, t_m * T_n + t_n) */
+  int32_t split_pieces;         /* pieces per split tile (0 when none is split) */
+  int32_t num_items;            /* queue entries: num_tiles + split_tiles * (split_pieces - 1) */
+  int32_t reserved[1];
 } agmm_config;
 
 typedef struct agmm_handle agmm_handle;
@@ -160,15 +169,22 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg);
 #define AGMM_Q_STATUS 5       /* uint32[4]: {status, workgroup, flag index, value seen} */
 #define AGMM_Q_UNITS 6        /* uint32[2 * num_units]: (m-tile, k-group) in fetch order */
 #define AGMM_Q_MTILES 7       /* uint32[T_m]: m-tile in GEMM order, bit 31 = read in place */
-#define AGMM_Q_QUEUES 8       /* uint32[16 + num_tiles]: 8 queue offsets, 8 queue lengths, then
-                                 the tile ids queue by queue (tile id q = position of its
-                                 m-tile in GEMM order * T_n + n-tile) */
+#define AGMM_Q_QUEUES 8       /* uint32[18 + num_items]: 9 queue offsets, 9 queue lengths (8
+                                 per-XCD queues, then the tail queue of split-tile pieces),
+                                 then the entries queue by queue: bits 0-23 tile id q
+                                 (position of its m-tile in GEMM order * T_n + n-tile), bits
+                                 24-27 piece, bits 28-31 pieces - 1 (0 = not split) */
+#define AGMM_Q_PARTIALS 9     /* float[split_tiles * split_pieces * block_m * block_n]: the
+                                 split tiles' fp32 partial sums of the last run, slot
+                                 (tile, piece); inside a slot, element i of accumulator group
+                                 (fm, fn, g) of thread tid at ((fm*FN + fn)*4 + g)*1024 +
+                                 tid*4 + i (FN = block_n / 64, 256 threads) */
 
 /* Trace events (debug). One record per fetched unit, per computed tile and per flag wait
  * of wave 0, after the per-workgroup event ids of the iris issue (wg_fetch, wg_gemm,
  * wg_gemm_wait). Timestamps are the GPU's constant 100 MHz real-time counter. */
 #define AGMM_EV_FETCH 1      /* id = unit index, a = m-tile, b = k-group */
-#define AGMM_EV_GEMM 2       /* id = tile index, a = m-tile, b = n-tile */
+#define AGMM_EV_GEMM 2       /* id = queue entry (tile id and piece, as in AGMM_Q_QUEUES), a = m-tile, b = n-tile */
 #define AGMM_EV_GEMM_WAIT 3  /* id = flag index, a = value seen, b = polls */
 
 typedef struct agmm_trace_rec {

@@ -50,6 +50,9 @@ class Geometry:
     direct_local: bool
     F: int          # fetcher workgroups (may be 0 when nothing is staged)
     W: int          # workgroups in the grid (fetchers included)
+    num_cus: int = 256      # compute units of the device
+    num_wgs_req: int = 0    # requested grid size (0 = one workgroup per compute unit)
+    tail_split: int = 0     # 1 = split the tail tiles along K (0: never)
 
     @property
     def M_s(self) -> int:
@@ -97,17 +100,55 @@ def gemm_tiles(g: Geometry) -> List[Tuple[int, int]]:
 
 
 N_QUEUES, SUPER_ROWS, COL_BLOCK = 8, 4, 8
+MAX_SPLIT = 4
+TILE_MASK = 0xFFFFFF
+
+
+def split_plan(g: Geometry) -> Tuple[int, int, int]:
+    """(split tiles, pieces per split tile, first split tile t_m * T_n + t_n).
+
+    Only when splitting is asked for (tail_split = 1). With Wg GEMM workgroups a last round holds num_tiles % Wg tiles; when that is at most
+    half of Wg (and there is at least one full round), those tiles -- the last ones in
+    t_m * T_n + t_n order -- are cut along K into S = min(4, Wg // tail, K-tiles // 16)
+    pieces, S >= 2; otherwise nothing is split."""
+    T = g.T_m * g.T_n
+    w_base = min(g.num_wgs_req or g.num_cus, g.num_cus)
+    wg = min(w_base, T)
+    kt = -(-g.K // g.BK)
+    if not g.tail_split or wg <= 0 or T <= wg or T > TILE_MASK:
+        return 0, 0, T
+    tail = T % wg
+    if tail == 0:
+        return 0, 0, T
+    S = min(MAX_SPLIT, wg // tail, kt // 16)
+    if S < 2:
+        return 0, 0, T
+    return tail, S, T - tail
+
+
+def entry(tile: int, piece: int = 0, pieces: int = 1) -> int:
+    return tile | (piece << 24) | ((pieces - 1) << 28)
 
 
 def tile_queues(g: Geometry) -> List[List[int]]:
-    """The per-XCD tile queues, as lists of tile ids q (q = GEMM position * T_n + n)."""
-    queues = [[] for _ in range(N_QUEUES)]
+    """The 8 per-XCD queues and the tail queue, as lists of entries (tile id q = GEMM
+    position * T_n + n, plus piece and piece count for split tiles)."""
+    tail, S, base = split_plan(g)
+    order = mtile_order(g)
+    pos_of = {t: i for i, t in enumerate(order)}
+    queues = [[] for _ in range(N_QUEUES + 1)]
     for j, s0 in enumerate(range(0, g.T_m, SUPER_ROWS)):
         rows = range(s0, min(g.T_m, s0 + SUPER_ROWS))
         for nb in range(0, g.T_n, COL_BLOCK):
             for pos in rows:
                 for n in range(nb, min(g.T_n, nb + COL_BLOCK)):
+                    if S and order[pos] * g.T_n + n >= base:
+                        continue
                     queues[j % N_QUEUES].append(pos * g.T_n + n)
+    for c in range(base, g.T_m * g.T_n if S else base):
+        q = pos_of[c // g.T_n] * g.T_n + c % g.T_n
+        for piece in range(S):
+            queues[N_QUEUES].append(entry(q, piece, S))
     return queues
 
 

@@ -82,18 +82,23 @@ def test_validation_errors(A):
 
 
 def test_workspace_bytes_large(A):
-    # 16384x3584x8192, D=8, tile 256: staging M*K fp16, flags T_m*G, counters (a done word,
-    # status words, 8 queue counters on their own 128-byte lines), 56 staged m-tiles x 8
-    # k-groups of 8-byte unit records, 64 m-tile records, 64*14 queue entries;
-    # 256-byte aligned pieces.
+    # 16384x3584x8192, D=8, tile 256 (sized for 256 compute units): staging M*K fp16, flags
+    # T_m*G, counters (a done word, status words, 9 queue counters on their own 128-byte
+    # lines), 128 split-tile counters (896 tiles = 3 rounds of 256 + 128, split in 2 along
+    # K), 56 staged m-tiles x 8 k-groups of 8-byte unit records, 64 m-tile records, 768 + 2 *
+    # 128 queue entries, 2 * 128 fp32 partial tiles; 256-byte aligned pieces.
     al = lambda x: (x + 255) & ~255
-    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al((32 + 8 * 32) * 4) + al(56 * 8 * 8)
-           + al(64 * 4) + al(64 * 14 * 4) + 0 + al(4))
-    got = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1)
+    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al((32 + 9 * 32) * 4) + al(128 * 4)
+           + al(56 * 8 * 8) + al(64 * 4) + al(1024 * 4) + al(256 * 256 * 256 * 4) + 0 + al(4))
+    got = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1,
+              tail_split=1)
     assert got == exp
     # direct_local off: all 64 m-tiles staged
-    got2 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, direct_local=0)
+    got2 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, direct_local=0, tail_split=1)
     assert got2 - got == al(64 * 8 * 8) - al(56 * 8 * 8)
+    # no tail split (the default): no counters, partial slots or extra queue entries
+    got3 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1)
+    assert got - got3 == al(128 * 4) - al(4) + al(1024 * 4) - al(896 * 4) + al(256 * 256 * 256 * 4)
     # D=1 with direct reads: nothing staged, no staging buffer
     assert _ws(A, D=1, M=1024, N=1024, K=1024, block_m=128) < 1 << 16
 

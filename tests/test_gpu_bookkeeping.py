@@ -3,6 +3,8 @@ schedule tables, final flag array, staging contents (staging poisoned with NaN f
 per-fetcher unit sequence, every output tile computed exactly once, every wait seeing the
 run's epoch. Also: stale-staging races (alternating inputs, poisoned staging), and the
 bounded flag wait (a unit whose flag the host never lets the fetcher publish)."""
+import itertools
+
 import numpy as np
 import pytest
 
@@ -19,13 +21,16 @@ CASES = [
              32, rank=0),
     Workload("bk_off", 2, 2 * 128, 384, 640, "f16", "uniform", False, "k_contiguous", False, 33,
              rank=1),
+    # 17 x 16 tiles of 64 with bm=64 (272 > 256 workgroups): the last 16 tiles split along K
+    Workload("bk_split", 2, 2 * 544, 1024, 2048, "f16", "normal_sqrtk", True, "m_contiguous",
+             True, 34, rank=1),
 ]
 
 
 def geometry(w, cfg):
     return sm.Geometry(w.D, w.M, w.N, w.K, cfg["block_m"], cfg["block_n"], cfg["block_k"],
                        cfg["k_per_flag"], w.rank, w.direct_local, cfg["num_fetch_wgs"],
-                       cfg["num_wgs"])
+                       cfg["num_wgs"], num_cus=cfg["num_cus"], tail_split=1)
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
@@ -38,12 +43,15 @@ def test_bookkeeping_matches_model(w, bm):
     g_in = inp.to("cuda")
     op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
                     direct_local=w.direct_local, has_bias=w.has_bias, debug=True, block_m=bm,
-                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096)
+                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096, tail_split=1)
     cfg = op.config.as_dict()
     g = geometry(w, cfg)
     # tables
     assert [tuple(u) for u in op.units()] == sm.fetch_units(g)
     assert op.queues() == sm.tile_queues(g)
+    assert (cfg["split_tiles"], cfg["split_pieces"]) == sm.split_plan(g)[:2]
+    if w.name == "bk_split" and bm == 64 and cfg["num_cus"] == 256:
+        assert cfg["split_tiles"] == 16
     mt = op.mtiles()
     assert [int(x & 0x7FFFFFFF) for x in mt] == sm.mtile_order(g)
     assert [bool(x >> 31) for x in mt] == [sm.is_direct(g, t) for t in sm.mtile_order(g)]
@@ -75,7 +83,8 @@ def test_bookkeeping_matches_model(w, bm):
                     assert (int(rec["a"]), int(rec["b"])) == sm.fetch_units(g)[rec["id"]]
                 elif rec["event"] == A.EV_GEMM:
                     tiles.append(int(rec["id"]))
-                    assert (int(rec["a"]), int(rec["b"])) == sm.gemm_tiles(g)[rec["id"]]
+                    tile = int(rec["id"]) & sm.TILE_MASK
+                    assert (int(rec["a"]), int(rec["b"])) == sm.gemm_tiles(g)[tile]
                 elif rec["event"] == A.EV_GEMM_WAIT:
                     assert int(rec["a"]) == epoch
                     t_m, kg = divmod(int(rec["id"]), g.G)
@@ -89,7 +98,8 @@ def test_bookkeeping_matches_model(w, bm):
                 seq = [posn[t] for t in mine if t in posn]
                 assert seq == sorted(seq)
         assert [fetched[f] for f in range(g.F)] == sm.fetcher_lists(g)
-        assert sorted(tiles) == list(range(len(sm.gemm_tiles(g))))
+        # every queue entry (tile, or piece of a split tile) computed exactly once
+        assert sorted(tiles) == sorted(itertools.chain(*sm.tile_queues(g)))
         assert np.array_equal(op.status(), np.zeros(4, dtype=np.uint32))
     op.close()
 

@@ -152,3 +152,56 @@ def test_full_size_exact_integer_sampled(w):
     C = oracle_sampled(wi, inp, rows, cols)
     import oracle
     assert np.array_equal(fo[rows, cols], oracle.encode_rne(wi.dtype, C))
+
+
+SPLIT = [
+    # (D, M_s, N, K, dtype, layout, bias, num_wgs): 17 x 16 tiles of 64, so with 256 (or 128)
+    # workgroups 16 tiles are left for a last round and split along K
+    (2, 544, 1024, 2048, "f16", "m_contiguous", True, 0),      # 4 pieces of 16 K-tiles
+    (2, 544, 1024, 2048, "bf16", "k_contiguous", False, 128),  # 4 pieces
+    (4, 272, 1024, 1024, "f16", "k_contiguous", True, 0),      # 2 pieces
+]
+
+
+@pytest.mark.parametrize("D,Ms,N,K,dt,layout,bias,nw", SPLIT)
+def test_tail_split_full_oracle(D, Ms, N, K, dt, layout, bias, nw):
+    """Tiles of the last round cut along K: every piece's partial sums go to the workspace
+    and the piece that completes the tile adds them in piece order. Output against the
+    oracle, fused == baseline bit for bit, identical over repeated runs (the per-tile piece
+    counters are epoch-valued), the same shape without splitting within tolerance, and
+    exact-integer inputs bit-exact."""
+    from oracle import schedule_model as sm
+    w = Workload(f"split_{D}x{Ms}_{N}_{K}_{dt}_{layout}_{nw}", D, D * Ms, N, K, dt,
+                 "normal_sqrtk", bias, layout, True, 200 + K + nw, rank=D - 1)
+    print(f"case {w.name}", flush=True)
+    kw = dict(block_m=64, num_fetch_wgs=8, tail_split=1)
+    if nw:
+        kw["num_wgs"] = nw
+    inp = make_inputs(w)
+    dev = inp.to("cuda")
+    C, _ = oracle_full(w, inp)
+    f = run_gpu(w, inp, "fused", keep=True, dev_inp=dev, **kw)
+    cfg = f.config
+    g = sm.Geometry(w.D, w.M, w.N, w.K, 64, 64, cfg["block_k"], cfg["k_per_flag"], w.rank, True,
+                    cfg["num_fetch_wgs"], cfg["num_wgs"], num_cus=cfg["num_cus"],
+                    num_wgs_req=nw, tail_split=1)
+    tail, S, _ = sm.split_plan(g)
+    assert (cfg["split_tiles"], cfg["split_pieces"]) == (tail, S)
+    if cfg["num_cus"] == 256:
+        assert tail == 16 and S == (2 if K == 1024 else 4)
+    fo = out_bits(f.out)
+    assert_close(w, fo, C, "fused")
+    for _ in range(2):  # later runs: the same bits
+        out = f.op.run(dev.shards, dev.B, dev.bias)
+        assert np.array_equal(out_bits(out), fo)
+    f.op.close()
+    bo = out_bits(run_gpu(w, inp, "baseline", dev_inp=dev, **kw).out)
+    assert np.array_equal(fo, bo)
+    nosplit = run_gpu(w, inp, "fused", dev_inp=dev, **dict(kw, tail_split=0))
+    assert nosplit.config["split_tiles"] == 0
+    assert_close(w, out_bits(nosplit.out), C, "fused, no split")
+    wi = w.with_(dist="int", name=w.name + "_int")
+    inpi = make_inputs(wi)
+    _, out16 = oracle_full(wi, inpi)
+    assert np.array_equal(out_bits(run_gpu(wi, inpi, "fused", **kw).out), out16)
+    assert np.array_equal(out_bits(run_gpu(wi, inpi, "baseline", **kw).out), out16)

@@ -60,7 +60,7 @@ def test_direct_local_off_stages_everything():
     (1, 64, 64, 64, 32, 32, 32, 1, 0, True, 0, 4),             # D=1: nothing staged
 ])
 def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
-    g = sm.Geometry(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W)
+    g = sm.Geometry(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W, num_wgs_req=W)
     tiles = sm.gemm_tiles(g)
     assert sorted(tiles) == sorted(itertools.product(range(g.T_m), range(g.T_n)))
     units = sm.fetch_units(g)
@@ -79,9 +79,8 @@ def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
         lists = sm.fetcher_lists(g)
         assert sorted(itertools.chain(*lists)) == list(range(len(units)))
         assert all(lst == sorted(lst) for lst in lists)
-    # queues partition the tiles
-    qs = sm.tile_queues(g)
-    assert sorted(itertools.chain(*qs)) == list(range(len(tiles)))
+    # queues partition the tiles; a split tile appears as its pieces, in the tail queue
+    check_queues_partition(g)
     # flags: exactly the staged units carry the epoch
     f = sm.expected_flags(g, 5)
     assert int((f == 5).sum()) == len(units)
@@ -90,6 +89,42 @@ def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
     for (t, kg), i in pos.items():
         if kg + 1 < g.G:
             assert pos[(t, kg + 1)] > i
+
+
+def check_queues_partition(g):
+    qs = sm.tile_queues(g)
+    tail, S, base = sm.split_plan(g)
+    T = g.T_m * g.T_n
+    order = sm.mtile_order(g)
+    split_q = {sm.mtile_order(g).index(c // g.T_n) * g.T_n + c % g.T_n for c in range(base, T)} \
+        if S else set()
+    regular = list(itertools.chain(*qs[:8]))
+    assert all(e >> 24 == 0 for e in regular)
+    assert sorted(regular + sorted(split_q)) == list(range(T))
+    assert sorted(qs[8]) == sorted(sm.entry(q, i, S) for q in split_q for i in range(S))
+    assert len(split_q) == tail
+    for q in split_q:  # split tiles are the last ones in t_m * T_n + t_n order
+        assert order[q // g.T_n] * g.T_n + q % g.T_n >= T - tail
+
+
+@pytest.mark.parametrize("T_m, T_n, K, cus, req, ts, exp", [
+    (64, 14, 8192, 256, 0, 1, (128, 2, 768)),    # 16384x3584 at 256x256 tiles: 3.5 rounds
+    (16, 18, 2048, 256, 0, 1, (32, 4, 256)),     # 288 tiles: 32 left over, 4 pieces of 16 K-tiles
+    (16, 18, 1024, 256, 0, 1, (32, 2, 256)),     # only 32 K-tiles: 2 pieces
+    (16, 18, 992, 256, 0, 1, (0, 0, 288)),       # 31 K-tiles: pieces would be under 16
+    (16, 16, 8192, 256, 0, 1, (0, 0, 256)),      # exactly one round
+    (16, 14, 8192, 256, 0, 1, (0, 0, 224)),      # fewer tiles than workgroups
+    (24, 16, 8192, 256, 0, 1, (128, 2, 256)),    # last round exactly half full: split in 2
+    (35, 11, 8192, 256, 0, 1, (0, 0, 385)),      # 129 left over: more than half, not split
+    (24, 15, 8192, 256, 0, 1, (104, 2, 256)),    # 360 tiles: 104 left over
+    (16, 18, 2048, 256, 70, 1, (8, 4, 280)),     # 70 workgroups requested: 288 % 70 = 8
+    (64, 14, 8192, 256, 0, 0, (0, 0, 896)),      # splitting not asked for (the default)
+])
+def test_split_plan_hand_examples(T_m, T_n, K, cus, req, ts, exp):
+    g = sm.Geometry(1, T_m * 32, T_n * 32, K, 32, 32, 32, 1, 0, True, 0, cus, num_cus=cus,
+                    num_wgs_req=req, tail_split=ts)
+    assert sm.split_plan(g) == exp
+    check_queues_partition(g)
 
 
 def test_expected_staging_layouts():
@@ -111,3 +146,4 @@ def test_queue_hand_example():
            [p * 10 + n for p in range(4) for n in range(8, 10)]
     exp1 = [p * 10 + n for p in (4, 5) for n in range(8)] + [p * 10 + n for p in (4, 5) for n in (8, 9)]
     assert q[0] == exp0 and q[1] == exp1 and all(not x for x in q[2:])
+    assert len(q) == 9  # eight XCD queues and the (empty) tail queue
