@@ -17,10 +17,15 @@
 // B, and A staged m_contiguous -- through the transposing ds_read_b64_tr_b16). One
 // barrier per K-tile; the output tile goes through LDS for 16-byte coalesced stores.
 //
-// Flag protocol: producer = every thread's agent-scope release fence (L2 write-back),
-// workgroup barrier, one agent-scope release store of the run's epoch. Consumer = relaxed
-// agent-scope polls with s_sleep backoff (the busy-wait back-off suggested in ROCm/iris PR
-// "Let's make Iris' All-reduce the best!"), then one agent-scope acquire fence. Every
+// Flag protocol: a unit of BM rows is fetched as BM / 64 pieces, by whichever workgroups
+// claim them; its flag counts published pieces and is complete at (BM / 64) * epoch.
+// Producer = every wave waits until its stores are acknowledged (they then sit in this
+// XCD's L2: the vector L1 writes through), workgroup barrier, then one agent-scope release
+// add by thread 0, whose L2 write-back publishes the whole workgroup's stores. Consumer =
+// wave 0 of the GEMM workgroup: relaxed agent-scope polls with s_sleep backoff (the
+// busy-wait back-off suggested in ROCm/iris PR "Let's make Iris' All-reduce the best!"),
+// then one agent-scope acquire fence for every flag it has seen complete; the other waves
+// request that data only after a later workgroup barrier. Every
 // wait is bounded by a spin limit; a timeout is recorded in the status word, the waiting
 // tile finishes on whatever staging holds (so every barrier is still met), and all
 // workgroups stop taking tiles, so the grid always drains.
@@ -252,14 +257,15 @@ __device__ inline bool aborted(const KParams& p) {
   return __hip_atomic_load(p.ctr + CTR_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-// Waits (every lane of the calling wave) until flags[idx] == epoch, then acquires.
-__device__ inline void wait_flag(const KParams& p, int64_t idx, Tracer& tr) {
+// Waits (every lane of the calling wave) until flags[idx] == target. No acquire: the caller
+// issues one for every flag it has seen complete.
+__device__ inline void poll_flag(const KParams& p, int64_t idx, uint32_t target, Tracer& tr) {
   uint32_t* f = p.flags + idx;
   const uint64_t t0 = tr.now();
   uint32_t polls = 0;
   uint32_t v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int backoff = 1;
-  while (v != p.epoch) {
+  while (v != target) {
     ++polls;
     if (polls >= p.spin_limit) {
       if ((threadIdx.x & 63) == 0 &&
@@ -278,7 +284,6 @@ __device__ inline void wait_flag(const KParams& p, int64_t idx, Tracer& tr) {
     if (backoff < 16) backoff <<= 1;
     v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   tr.rec(AGMM_EV_GEMM_WAIT, (uint32_t)idx, v, polls, t0);
 }
 
@@ -360,14 +365,76 @@ __device__ inline int grab(const KParams& p);
 // piece / pieces: a split tile's piece covers K-tiles [piece * KT / pieces, (piece + 1) * KT /
 // pieces); its fp32 partial sums go to a workspace slot and the piece that finishes the tile
 // last adds all of them in piece order (so the sum does not depend on which piece ends
-// last) and runs the epilogue. is_last: an LDS word for that decision.
-template <class T, int DT, bool A_KMAJOR, bool WAIT>
+// last) and runs the epilogue. is_last: an LDS word for that decision (and, at the tile's
+// start, for the workgroup's decision to keep fetching).
+//
+// help (fused mode): claims one fetch piece and copies it, false when none is left. Every
+// tile starts by fetching p.tile_pieces pieces, and a staged tile whose first k-group is not
+// published yet keeps fetching instead of sleeping; the fetcher workgroups (which never
+// wait) guarantee that every piece is claimed.
+template <class T, int DT, bool A_KMAJOR, bool WAIT, class Help>
 __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n,
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
-                                                         int tid, Tracer& tr, int* next_tile,
-                                                         int* is_last) {
+                                                         int tid_in, Tracer& tr, int* next_tile,
+                                                         int* is_last, Help&& help) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
+  // this piece's K-tiles [kt_lo, kt_lo + KT)
+  const int KT_all = (int)((p.K + BK - 1) / BK);
+  const int kt_lo = piece * KT_all / pieces;
+  const int KT = (piece + 1) * KT_all / pieces - kt_lo;
+  const int64_t fbase = (int64_t)t_m * p.G;
+  bool waits = WAIT && staged;
+  const int kpf = p.kpf;
+  const uint32_t target = (uint32_t)(BM / kPieceRows) * p.epoch;  // a published unit's flag
+  auto flag_of = [&](int g) {
+    return uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT));
+  };
+  // Consumer side of the flags. An agent-scope acquire invalidates the XCD's L2 (which all
+  // workgroups on that XCD rely on for operand reuse) and drains the wave's DMA requests in
+  // flight, so acquires are few: only wave 0 polls and acquires, and each acquire also
+  // takes every later k-group of the tile that is published already (once the fetchers are
+  // ahead, that is all of them). The other waves issue their requests for a k-group only
+  // after a workgroup barrier that wave 0 reaches after its acquire has completed, and they
+  // read through the same L1 and L2. ready_to: k-groups below it are acquired.
+  const bool wave0 = __builtin_amdgcn_readfirstlane(tid_in >> 6) == 0;
+  const int g_end = (kt_lo + KT + kpf - 1) / kpf;  // one past this piece's last k-group
+  int ready_to = kt_lo / kpf;
+  // wave 0: wait for k-groups ready_to .. g_need, take the published ones after them, acquire
+  auto acquire_groups = [&](int g_need) {
+    for (int g = ready_to; g <= g_need; ++g) poll_flag(p, fbase + g, target, tr);
+    int g = g_need + 1;
+    while (g < g_end && flag_of(g) == target) ++g;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    ready_to = g;
+  };
+  // Fetching for others happens here, before any of the tile's addressing state is live.
+  if constexpr (WAIT) {
+    for (int i = 0; i < p.tile_pieces; ++i)
+      if (!help()) break;
+    if (waits) {
+      // While the first k-group is not published, fetch for others (until nothing is left
+      // to claim; the K loop then waits as usual). help() has barriers, so thread 0 reads
+      // the flag and decides for the whole workgroup: waves that read the flag themselves
+      // could see different values and run different barrier sequences.
+      for (;;) {
+        if (tid_in == 0) *is_last = flag_of(kt_lo / kpf) != target;
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(*is_last) || !help()) break;
+      }
+      // every wave requests the first four K-tiles before the K loop's first barrier: wave 0
+      // acquires their k-groups first, this barrier orders the requests after it
+      if (wave0 && KT > 0) acquire_groups((kt_lo + min(KT - 1, 3)) / kpf);
+      __syncthreads();
+      waits = ready_to < g_end;
+    }
+  }
+  // The thread index through an empty asm: everything derived from it below (lane offsets,
+  // swizzles) is then computed per tile instead of being kept live across the whole tile
+  // loop, where the fetch above needs the registers.
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN;
   const int rows_valid = (int)min((int64_t)BM, p.M - m0);
@@ -394,10 +461,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   const uint16_t* bbase = p.B + n0;
   int64_t b_bytes = (p.K * p.N - n0) * 2;
   const int64_t b_step = (int64_t)BK * p.N;
-  // this piece's K-tiles [kt_lo, kt_lo + KT): the operand bases start at kt_lo
-  const int KT_all = (int)((p.K + BK - 1) / BK);
-  const int kt_lo = piece * KT_all / pieces;
-  const int KT = (piece + 1) * KT_all / pieces - kt_lo;
+  // the operand bases start at K-tile kt_lo
   abase += kt_lo * a_step;
   a_bytes -= kt_lo * a_step * 2;
   bbase += kt_lo * b_step;
@@ -424,24 +488,6 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) acc[fm][fn] = (f32x16)(0.0f);
 
-  const int64_t fbase = (int64_t)t_m * p.G;
-  bool waits = WAIT && staged;
-  const int kpf = p.kpf;
-  // A poll inside the K loop drains this wave's DMA requests in flight (vector loads
-  // complete in order), so first look at every k-group's flag while the pipeline is still
-  // empty: when all are published already (the usual case once the fetchers are ahead),
-  // one acquire covers the whole tile and the K loop polls nothing.
-  if (waits) {
-    bool all = true;
-    for (int g = kt_lo / kpf; g * kpf < kt_lo + KT && all; ++g)
-      all = uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT)) == p.epoch;
-    if (all) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      waits = false;
-    }
-  }
-
   // This tile's bias slice to LDS (read after the K loop's barriers).
   // (zeros without a bias: the epilogue then has no branch, which would otherwise make the
   // compiler move every accumulator out of the AGPRs at once and spill)
@@ -456,13 +502,14 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     rsrc_t ra, rb;
     int64_t k_rem;
   };
-  // Fused mode: wait for every staged k-group whose first K-tile lies in [lo, hi] (K-tiles
-  // of this piece). Called once per block of four K-tiles, before the block that requests
-  // them, so the polling code stays outside the unrolled MFMA stream.
-  auto wait_range = [&](int lo, int hi) {
-    if (!waits) return;
-    for (int g = (kt_lo + lo + kpf - 1) / kpf; g * kpf <= kt_lo + hi; ++g)
-      wait_flag(p, fbase + g, tr);
+  // Fused mode: make the staged k-groups of K-tiles up to hi (of this piece) available.
+  // Called once per block of four K-tiles, before the block that requests them (their
+  // requests follow a K-loop barrier), so the polling stays outside the MFMA stream; only
+  // wave 0 acts, and only when the block reaches a k-group it has not acquired yet.
+  auto wait_range = [&](int hi) {
+    if (!waits || !wave0) return;
+    const int g_need = (kt_lo + hi) / kpf;
+    if (g_need >= ready_to) acquire_groups(g_need);
   };
   auto resources = [&](int t) -> Req {
     const int64_t ka = t * a_step, kb = t * b_step;
@@ -564,9 +611,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   using NO = std::false_type;
 
   if (KT > 0) {
-    if (waits && kt_lo % kpf != 0) wait_flag(p, fbase + kt_lo / kpf, tr);  // group begun earlier
-    wait_range(0, min(KT - 1, 3));
-    request(0, st.off[0]);
+    request(0, st.off[0]);  // k-groups of K-tiles 0..3 acquired before the tile's barrier
     if (KT > 1) request(1, st.off[1]);
     if (KT > 2) request(2, st.off[2]);
     if (KT > 3) {  // the A slice only: step 0 requests the B slice
@@ -588,14 +633,14 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     for (int r = 0; r < NR; ++r) read_one(r, st.s[0], 0, fa[0], fb[0]);
     int t = 0;
     for (; t + 8 <= KT; t += 4) {
-      wait_range(t + 4, t + 7);
+      wait_range(t + 7);
       step(I0{}, YES{}, t);
       step(I1{}, YES{}, t + 1);
       step(I2{}, YES{}, t + 2);
       step(I3{}, YES{}, t + 3);
     }
     if (t + 4 <= KT) {
-      wait_range(t + 4, KT - 1);
+      wait_range(KT - 1);
       step(I0{}, NO{}, t);
       step(I1{}, NO{}, t + 1);
       step(I2{}, NO{}, t + 2);
@@ -777,9 +822,9 @@ struct UnitRows {
 // kFetchDepth loads stay in flight.
 template <int BM>
 __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
-                                 int KG, int tid) {
-  const int64_t m_beg = (int64_t)t_m * BM;
-  const int R = (int)min((int64_t)BM, p.M - m_beg);
+                                 int KG, int tid, int row0, int nrows) {
+  const int64_t m_beg = (int64_t)t_m * BM + row0;
+  const int R = (int)min((int64_t)nrows, p.M - m_beg);
   const int64_t k_beg = (int64_t)g * KG;
   const int CR = (int)(min((int64_t)KG, p.K - k_beg) / 8);
   if (CR <= 0 || R <= 0) return;
@@ -829,10 +874,10 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
 // buffer-access fast path as the k_contiguous copy.
 template <int BM>
 __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
-                                 int KG, int tid) {
+                                 int KG, int tid, int row0, int nrows) {
   constexpr int NB = kFetchDepth / 8;  // blocks per thread in flight
-  const int64_t m_beg = (int64_t)t_m * BM;
-  const int R = (int)min((int64_t)BM, p.M - m_beg);       // multiple of 8
+  const int64_t m_beg = (int64_t)t_m * BM + row0;
+  const int R = (int)min((int64_t)nrows, p.M - m_beg);    // multiple of 8
   const int64_t k_beg = (int64_t)g * KG;
   const int NBK = (int)(min((int64_t)KG, p.K - k_beg) / 8);
   const int NBM = R / 8;
@@ -894,27 +939,65 @@ __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards
   }
 }
 
-// Units f, f+F, f+2F, ... of the fetch order. publish: fused mode, set each unit's flag.
-template <class T, bool LAYOUT_K>
-__device__ void fetch_loop(const KParams& p, const uint16_t* const* shards, int f, int F,
-                           bool publish, Tracer& tr, int tid) {
+// Baseline copy: units f, f+F, f+2F, ... of the fetch order, whole units, no flags.
+template <class T>
+__device__ void copy_units(const KParams& p, const uint16_t* const* shards, int f, int F, int tid) {
   const int KG = p.kpf * T::BK;
   for (int u = f; u < p.num_units; u += F) {
     const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
-    const uint64_t t0 = tr.now();
-    if (LAYOUT_K)
-      copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid);
-    else
-      copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid);
-    if (publish) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0 && u != p.skip_unit)
-        __hip_atomic_store(p.flags + (int64_t)t_m * p.G + g, p.epoch, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    tr.rec(AGMM_EV_FETCH, (uint32_t)u, (uint32_t)t_m, (uint32_t)g, t0);
+    copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
   }
+}
+
+// Fused mode: fetch pieces [pc, pc + n) (piece pc is rows kPieceRows * (pc % PPU) .. of
+// unit pc / PPU, PPU = BM / kPieceRows; n <= PPU, so at most two units), then publish them:
+// each wave waits for its stores, a workgroup barrier, and thread 0 adds each unit's count
+// of pieces to its flag with one agent-scope release (a single L2 write-back per unit
+// instead of one per wave: a write-back flushes the XCD's whole L2, which the GEMM
+// workgroups beside this one are using).
+template <class T, bool LAYOUT_K>
+__device__ __attribute__((always_inline)) void fetch_pieces(const KParams& p,
+                                                            const uint16_t* const* shards,
+                                                            int pc, int n, int tid, Tracer& tr) {
+  constexpr int PPU = T::BM / kPieceRows;
+  const int KG = p.kpf * T::BK;
+  const uint64_t t0 = tr.now();
+  for (int i = 0; i < n;) {
+    const int u = (pc + i) / PPU, sub = (pc + i) - u * PPU, cnt = min(n - i, PPU - sub);
+    const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
+    if (LAYOUT_K)
+      copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, sub * kPieceRows, cnt * kPieceRows);
+    else
+      copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid, sub * kPieceRows, cnt * kPieceRows);
+    i += cnt;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 0; i < n;) {
+      const int u = (pc + i) / PPU, sub = (pc + i) - u * PPU, cnt = min(n - i, PPU - sub);
+      const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
+      if (u != p.skip_unit)
+        __hip_atomic_fetch_add(p.flags + (int64_t)t_m * p.G + g, (uint32_t)cnt, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < cnt; ++j)
+        tr.rec(AGMM_EV_FETCH, (uint32_t)(pc + i + j), (uint32_t)t_m, (uint32_t)g, t0);
+      i += cnt;
+    }
+  }
+}
+
+// Claims the next n fetch pieces for the workgroup: returns the first and sets *n to how
+// many of them exist (0: none left). slot: an LDS word; the caller's next claim comes after
+// a barrier (fetch_pieces has one).
+__device__ inline int claim_pieces(const KParams& p, int* slot, int tid, int& n) {
+  if (tid == 0)
+    *slot = aborted(p) ? p.num_pieces
+                       : (int)min((uint32_t)p.num_pieces, atomicAdd(p.ctr + CTR_FETCH, (uint32_t)n));
+  __syncthreads();
+  const int pc = __builtin_amdgcn_readfirstlane(*slot);
+  n = min(n, p.num_pieces - pc);
+  return pc;
 }
 
 // Next queue entry for this workgroup, or -1: its XCD's queue first, then the other XCD
@@ -951,16 +1034,36 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   st.off[1] = (uint32_t)(size_t)(lds_void*)lds1;
   st.off[2] = (uint32_t)(size_t)(lds_void*)lds2;
   st.off[3] = (uint32_t)(size_t)(lds_void*)lds3;
-  __shared__ int s_next, s_last;
+  __shared__ int s_next, s_last, s_claim;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
   Tracer tr{p.debug ? p.trace + (size_t)wg * p.trace_cap : nullptr, 0u, (uint32_t)p.trace_cap,
             p.debug != 0};
 
-  if (FUSED && wg < p.F) {
+  if constexpr (FUSED) {
     load_shard_table(p, s_shards, tid);
-    fetch_loop<T, LAYOUT_K>(p, s_shards, wg, p.F, true, tr, tid);
+    if (wg < p.F) {  // fetcher: claim a unit's worth of pieces at a time until none is left,
+                     // then compute like the rest
+      for (;;) {
+        int n = T::BM / kPieceRows;
+        const int pc = claim_pieces(p, &s_claim, tid, n);
+        if (n <= 0) break;
+        fetch_pieces<T, LAYOUT_K>(p, s_shards, pc, n, tid, tr);
+      }
+    }
   }
+
+  auto help = [&]() -> bool {
+    if constexpr (FUSED) {
+      int n = 1;
+      const int pc = claim_pieces(p, &s_claim, tid, n);
+      if (n <= 0) return false;
+      fetch_pieces<T, LAYOUT_K>(p, s_shards, pc, n, tid, tr);
+      return true;
+    } else {
+      return false;
+    }
+  };
 
   if (tid == 0) s_next = grab(p);
   __syncthreads();
@@ -975,14 +1078,14 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
     } else if constexpr (LAYOUT_K) {
-      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
     } else {
       if (!staged)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     __syncthreads();
@@ -996,6 +1099,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
       for (int x = 0; x < kQueueSlots; ++x)
         __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -1005,9 +1109,8 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
 template <int BM>
 __global__ __launch_bounds__(kThreads) void agmm_copy(KParams p) {
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
-  Tracer tr{nullptr, 0u, 0u, false};
   load_shard_table(p, s_shards, threadIdx.x);
-  fetch_loop<Tile<BM>, true>(p, s_shards, blockIdx.x, gridDim.x, false, tr, threadIdx.x);
+  copy_units<Tile<BM>>(p, s_shards, blockIdx.x, gridDim.x, threadIdx.x);
 }
 
 __global__ void fill16_kernel(uint16_t* dst, int64_t n, uint16_t v) {
