@@ -158,7 +158,11 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   }
   c.block_m = c.block_n = bm;
   c.block_k = agmm::kBlockK;
-  c.k_per_flag = d.k_per_flag ? d.k_per_flag : std::max(1, 1024 / c.block_k);
+  // k-group: 1024 K columns (the pages' default), or 512 once K >= 4096. Measured on one
+  // MI355X: tiles of a one-round grid start as soon as the first k-group of their m-tile
+  // arrives, and a smaller first group arrives sooner; with short K, finer groups catch up
+  // with the fetch front and cost more acquires than they save.
+  c.k_per_flag = d.k_per_flag ? d.k_per_flag : std::max(1, (d.K >= 4096 ? 512 : 1024) / c.block_k);
   const int64_t KG = (int64_t)c.k_per_flag * c.block_k;
   const int64_t T_m = cdiv(d.M, bm), T_n = cdiv(d.N, bm);
   const int64_t G = d.K > 0 ? cdiv(d.K, KG) : 0;
@@ -207,8 +211,15 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   pl->split_base = c.num_tiles - tail;
 
   // Grid: one workgroup per CU (a 128 KiB LDS footprint allows one), fetchers first.
+  // Fetchers: the default count, unless every tile runs in the first round and fewer
+  // workgroups than that are left over: then every fetcher would hold back a tile for the
+  // whole fetch, and one fetcher per unit finishes the fetch in one pass instead.
   int F = 0;
-  if (n_units > 0) F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
+  if (n_units > 0) {
+    F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
+    if (!d.num_fetch_wgs && c.num_items <= W_base && W_base - c.num_items < kDefaultFetchWgs)
+      F = (int)std::min<int64_t>(n_units, W_base);
+  }
   F = (int)std::min<int64_t>(F, n_units);
   int64_t W = W_base;                                  // every workgroup resident
   W = std::min<int64_t>(W, (int64_t)F + c.num_items);  // no idle workgroups

@@ -76,8 +76,11 @@ typedef struct agmm_desc {
   int32_t debug;         /* 1: record per-workgroup trace; run() synchronizes and reports
                             a flag-wait timeout as AGMM_ERR_TIMEOUT */
   int32_t block_m;       /* output tile edge: 64, 128 or 256 (tile is square); 0 = auto */
-  int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto (1024 columns) */
-  int32_t num_fetch_wgs; /* fetcher workgroups (fused); 0 = auto */
+  int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto (512 columns when
+                            K >= 4096, else 1024) */
+  int32_t num_fetch_wgs; /* fetcher workgroups (fused); 0 = auto: 32, or one per fetch unit
+                            when all tiles fit in one round with fewer than 32 workgroups
+                            to spare */
   int32_t num_wgs;       /* workgroups in the persistent grid; 0 = one per compute unit */
   int32_t trace_cap;     /* debug trace records per workgroup; 0 = auto */
   uint32_t spin_limit;   /* flag polls before a wait gives up; 0 = auto (several seconds) */

@@ -84,20 +84,20 @@ def test_validation_errors(A):
 
 
 def test_workspace_bytes_large(A):
-    # 16384x3584x8192, D=8, tile 256 (sized for 256 compute units): staging M*K fp16, flags
-    # T_m*G, counters (a done word and status words, the fetch-piece counter and 9 queue
+    # 16384x3584x8192, D=8, tile 256 (sized for 256 compute units), k-groups of 512 columns
+    # (the default once K >= 4096, so G = 16): staging M*K fp16, flags T_m*G, counters (a done word and status words, the fetch-piece counter and 9 queue
     # counters, each on its own 128-byte line), 128 split-tile counters (896 tiles = 3 rounds of 256 + 128, split in 2 along
-    # K), 56 staged m-tiles x 8 k-groups of 8-byte unit records, 64 m-tile records, 768 + 2 *
+    # K), 56 staged m-tiles x 16 k-groups of 8-byte unit records, 64 m-tile records, 768 + 2 *
     # 128 queue entries, 2 * 128 fp32 partial tiles; 256-byte aligned pieces.
     al = lambda x: (x + 255) & ~255
-    exp = (al(16384 * 8192 * 2) + al(64 * 8 * 4) + al((96 + 9 * 32) * 4) + al(128 * 4)
-           + al(56 * 8 * 8) + al(64 * 4) + al(1024 * 4) + al(256 * 256 * 256 * 4) + 0 + al(4))
+    exp = (al(16384 * 8192 * 2) + al(64 * 16 * 4) + al((96 + 9 * 32) * 4) + al(128 * 4)
+           + al(56 * 16 * 8) + al(64 * 4) + al(1024 * 4) + al(256 * 256 * 256 * 4) + 0 + al(4))
     got = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1,
               tail_split=1)
     assert got == exp
     # direct_local off: all 64 m-tiles staged
     got2 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, direct_local=0, tail_split=1)
-    assert got2 - got == al(64 * 8 * 8) - al(56 * 8 * 8)
+    assert got2 - got == al(64 * 16 * 8) - al(56 * 16 * 8)
     # no tail split (the default): no counters, partial slots or extra queue entries
     got3 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, layout=A.M_CONTIGUOUS, has_bias=1)
     assert got - got3 == al(128 * 4) - al(4) + al(1024 * 4) - al(896 * 4) + al(256 * 256 * 256 * 4)
