@@ -50,7 +50,7 @@ class agmm_desc(ctypes.Structure):
         ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
         ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
-        ("tile_pieces", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -65,7 +65,6 @@ class agmm_config(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
         ("split_pieces", ctypes.c_int32), ("num_items", ctypes.c_int32),
-        ("tile_pieces", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -75,7 +75,6 @@ int validate_desc(const agmm_desc* d) {
     return AGMM_ERR_INVALID_ARG;
   if (d->debug_skip_unit < -1) return AGMM_ERR_INVALID_ARG;
   if (d->tail_split != 0 && d->tail_split != 1) return AGMM_ERR_INVALID_ARG;
-  if (d->tile_pieces < 0) return AGMM_ERR_INVALID_ARG;
   if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
   if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
     return AGMM_ERR_UNSUPPORTED;
@@ -228,9 +227,6 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   c.num_fetch_wgs = F;
   c.num_wgs = (int32_t)W;
   c.num_copy_wgs = (int32_t)std::min<int64_t>(n_units, 4LL * num_cus);
-  const int64_t n_pieces = n_units * (bm / agmm::kPieceRows);
-  if (n_pieces >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
-  c.tile_pieces = d.tile_pieces;
 
   // Fetch order: staged m-tiles in GEMM order, in windows of the m-tiles the grid works on
   // at once; inside a window, k-group by k-group.
@@ -485,8 +481,6 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   p.G = c.G;
   p.kpf = c.k_per_flag;
   p.num_units = c.num_units;
-  p.num_pieces = c.num_units * (c.block_m / agmm::kPieceRows);
-  p.tile_pieces = c.tile_pieces;
   p.num_tiles = c.num_tiles;
   p.epoch = epoch;
   p.debug = d.debug;

@@ -28,7 +28,6 @@ constexpr int kMaxSplit = 4;
 // A fetch unit (m-tile x k-group) is copied in pieces of kPieceRows rows, claimed one by
 // one from a global counter; a unit's flag counts its finished pieces (BM / kPieceRows per
 // run, so after run e it holds e * BM / kPieceRows).
-constexpr int kPieceRows = 64;
 
 // Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
 enum : int {
@@ -37,7 +36,7 @@ enum : int {
   CTR_STATUS_WG = 3,    // workgroup that timed out
   CTR_STATUS_FLAG = 4,  // flag index it waited on
   CTR_STATUS_SEEN = 5,  // flag value it last saw
-  CTR_FETCH = 64,       // next fetch piece to claim (own 128-byte line)
+  CTR_FETCH = 64,       // next fetch unit to claim (own 128-byte line)
   CTR_Q = 96,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
   CTR_QSTRIDE = 32,
   CTR_WORDS = CTR_Q + kQueueSlots * CTR_QSTRIDE
@@ -64,8 +63,6 @@ struct KParams {
   int64_t M, N, K, M_s;
   int32_t D, rank, T_m, T_n, G, kpf;
   int32_t num_units, num_tiles, F;
-  int32_t num_pieces;       // num_units * BM / kPieceRows
-  int32_t tile_pieces;      // pieces a GEMM workgroup claims at the start of each tile
   int32_t staged_kmajor;    // 1: staging is [M][K]; 0: staging is [K][M]
   uint32_t epoch;
   int32_t debug, trace_cap;

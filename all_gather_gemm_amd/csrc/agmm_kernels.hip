@@ -17,11 +17,11 @@
 // B, and A staged m_contiguous -- through the transposing ds_read_b64_tr_b16). One
 // barrier per K-tile; the output tile goes through LDS for 16-byte coalesced stores.
 //
-// Flag protocol: a unit of BM rows is fetched as BM / 64 pieces, by whichever workgroups
-// claim them; its flag counts published pieces and is complete at (BM / 64) * epoch.
-// Producer = every wave waits until its stores are acknowledged (they then sit in this
-// XCD's L2: the vector L1 writes through), workgroup barrier, then one agent-scope release
-// add by thread 0, whose L2 write-back publishes the whole workgroup's stores. Consumer =
+// Flag protocol: fetcher workgroups claim units from one counter; a unit's flag holds the
+// run's epoch once the unit is in staging. Producer = every wave waits until its stores
+// are acknowledged (they then sit in this XCD's L2: the vector L1 writes through),
+// workgroup barrier, then one agent-scope release add of 1 by thread 0, whose L2 write-back
+// publishes the whole workgroup's stores. Consumer =
 // wave 0 of the GEMM workgroup: relaxed agent-scope polls with s_sleep backoff (the
 // busy-wait back-off suggested in ROCm/iris PR "Let's make Iris' All-reduce the best!"),
 // then one agent-scope acquire fence for every flag it has seen complete; the other waves
@@ -365,19 +365,14 @@ __device__ inline int grab(const KParams& p);
 // piece / pieces: a split tile's piece covers K-tiles [piece * KT / pieces, (piece + 1) * KT /
 // pieces); its fp32 partial sums go to a workspace slot and the piece that finishes the tile
 // last adds all of them in piece order (so the sum does not depend on which piece ends
-// last) and runs the epilogue. is_last: an LDS word for that decision (and, at the tile's
-// start, for the workgroup's decision to keep fetching).
+// last) and runs the epilogue. is_last: an LDS word for that decision.
 //
-// help (fused mode): claims one fetch piece and copies it, false when none is left. Every
-// tile starts by fetching p.tile_pieces pieces, and a staged tile whose first k-group is not
-// published yet keeps fetching instead of sleeping; the fetcher workgroups (which never
-// wait) guarantee that every piece is claimed.
-template <class T, int DT, bool A_KMAJOR, bool WAIT, class Help>
+template <class T, int DT, bool A_KMAJOR, bool WAIT>
 __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n,
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
                                                          int tid_in, Tracer& tr, int* next_tile,
-                                                         int* is_last, Help&& help) {
+                                                         int* is_last) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   // this piece's K-tiles [kt_lo, kt_lo + KT)
   const int KT_all = (int)((p.K + BK - 1) / BK);
@@ -386,7 +381,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   const int64_t fbase = (int64_t)t_m * p.G;
   bool waits = WAIT && staged;
   const int kpf = p.kpf;
-  const uint32_t target = (uint32_t)(BM / kPieceRows) * p.epoch;  // a published unit's flag
+  const uint32_t target = p.epoch;  // a published unit's flag
   auto flag_of = [&](int g) {
     return uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT));
@@ -409,25 +404,14 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     ready_to = g;
   };
-  // Fetching for others happens here, before any of the tile's addressing state is live.
   if constexpr (WAIT) {
-    for (int i = 0; i < p.tile_pieces; ++i)
-      if (!help()) break;
     if (waits) {
-      // While the first k-group is not published, fetch for others (until nothing is left
-      // to claim; the K loop then waits as usual). help() has barriers, so thread 0 reads
-      // the flag and decides for the whole workgroup: waves that read the flag themselves
-      // could see different values and run different barrier sequences.
-      for (;;) {
-        if (tid_in == 0) *is_last = flag_of(kt_lo / kpf) != target;
-        __syncthreads();
-        if (!__builtin_amdgcn_readfirstlane(*is_last) || !help()) break;
-      }
       // every wave requests the first four K-tiles before the K loop's first barrier: wave 0
       // acquires their k-groups first, this barrier orders the requests after it
       if (wave0 && KT > 0) acquire_groups((kt_lo + min(KT - 1, 3)) / kpf);
       __syncthreads();
-      waits = ready_to < g_end;
+      // only wave 0 waits for the rest; the other waves never poll and need no flag state
+      waits = wave0 && ready_to < g_end;
     }
   }
   // The thread index through an empty asm: everything derived from it below (lane offsets,
@@ -949,55 +933,39 @@ __device__ void copy_units(const KParams& p, const uint16_t* const* shards, int 
   }
 }
 
-// Fused mode: fetch pieces [pc, pc + n) (piece pc is rows kPieceRows * (pc % PPU) .. of
-// unit pc / PPU, PPU = BM / kPieceRows; n <= PPU, so at most two units), then publish them:
-// each wave waits for its stores, a workgroup barrier, and thread 0 adds each unit's count
-// of pieces to its flag with one agent-scope release (a single L2 write-back per unit
-// instead of one per wave: a write-back flushes the XCD's whole L2, which the GEMM
-// workgroups beside this one are using).
+// Fused mode: copy unit u into staging, then publish it: each wave waits for its stores,
+// a workgroup barrier, and thread 0 adds 1 to the unit's flag with one agent-scope release
+// (a single L2 write-back for the workgroup instead of one per wave: a write-back flushes
+// the XCD's whole L2, which the GEMM workgroups beside this one are using).
 template <class T, bool LAYOUT_K>
-__device__ __attribute__((always_inline)) void fetch_pieces(const KParams& p,
-                                                            const uint16_t* const* shards,
-                                                            int pc, int n, int tid, Tracer& tr) {
-  constexpr int PPU = T::BM / kPieceRows;
+__device__ __attribute__((always_inline)) void fetch_unit(const KParams& p,
+                                                          const uint16_t* const* shards, int u,
+                                                          int tid, Tracer& tr) {
   const int KG = p.kpf * T::BK;
   const uint64_t t0 = tr.now();
-  for (int i = 0; i < n;) {
-    const int u = (pc + i) / PPU, sub = (pc + i) - u * PPU, cnt = min(n - i, PPU - sub);
-    const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
-    if (LAYOUT_K)
-      copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, sub * kPieceRows, cnt * kPieceRows);
-    else
-      copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid, sub * kPieceRows, cnt * kPieceRows);
-    i += cnt;
-  }
+  const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
+  if (LAYOUT_K)
+    copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
+  else
+    copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
   wait_vmcnt<0>();
   __syncthreads();
   if (tid == 0) {
-    for (int i = 0; i < n;) {
-      const int u = (pc + i) / PPU, sub = (pc + i) - u * PPU, cnt = min(n - i, PPU - sub);
-      const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
-      if (u != p.skip_unit)
-        __hip_atomic_fetch_add(p.flags + (int64_t)t_m * p.G + g, (uint32_t)cnt, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      for (int j = 0; j < cnt; ++j)
-        tr.rec(AGMM_EV_FETCH, (uint32_t)(pc + i + j), (uint32_t)t_m, (uint32_t)g, t0);
-      i += cnt;
-    }
+    if (u != p.skip_unit)
+      __hip_atomic_fetch_add(p.flags + (int64_t)t_m * p.G + g, 1u, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    tr.rec(AGMM_EV_FETCH, (uint32_t)u, (uint32_t)t_m, (uint32_t)g, t0);
   }
 }
 
-// Claims the next n fetch pieces for the workgroup: returns the first and sets *n to how
-// many of them exist (0: none left). slot: an LDS word; the caller's next claim comes after
-// a barrier (fetch_pieces has one).
-__device__ inline int claim_pieces(const KParams& p, int* slot, int tid, int& n) {
+// Claims the next fetch unit for the workgroup (>= p.num_units: none left). slot: an LDS
+// word; the caller's next claim comes after a barrier (fetch_unit has one).
+__device__ inline int claim_unit(const KParams& p, int* slot, int tid) {
   if (tid == 0)
-    *slot = aborted(p) ? p.num_pieces
-                       : (int)min((uint32_t)p.num_pieces, atomicAdd(p.ctr + CTR_FETCH, (uint32_t)n));
+    *slot = aborted(p) ? p.num_units
+                       : (int)min((uint32_t)p.num_units, atomicAdd(p.ctr + CTR_FETCH, 1u));
   __syncthreads();
-  const int pc = __builtin_amdgcn_readfirstlane(*slot);
-  n = min(n, p.num_pieces - pc);
-  return pc;
+  return __builtin_amdgcn_readfirstlane(*slot);
 }
 
 // Next queue entry for this workgroup, or -1: its XCD's queue first, then the other XCD
@@ -1042,28 +1010,15 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
 
   if constexpr (FUSED) {
     load_shard_table(p, s_shards, tid);
-    if (wg < p.F) {  // fetcher: claim a unit's worth of pieces at a time until none is left,
-                     // then compute like the rest
+    if (wg < p.F) {  // fetcher: claim units until none is left, then compute like the rest
       for (;;) {
-        int n = T::BM / kPieceRows;
-        const int pc = claim_pieces(p, &s_claim, tid, n);
-        if (n <= 0) break;
-        fetch_pieces<T, LAYOUT_K>(p, s_shards, pc, n, tid, tr);
+        const int u = claim_unit(p, &s_claim, tid);
+        if (u >= p.num_units) break;
+        fetch_unit<T, LAYOUT_K>(p, s_shards, u, tid, tr);
       }
     }
   }
 
-  auto help = [&]() -> bool {
-    if constexpr (FUSED) {
-      int n = 1;
-      const int pc = claim_pieces(p, &s_claim, tid, n);
-      if (n <= 0) return false;
-      fetch_pieces<T, LAYOUT_K>(p, s_shards, pc, n, tid, tr);
-      return true;
-    } else {
-      return false;
-    }
-  };
 
   if (tid == 0) s_next = grab(p);
   __syncthreads();
@@ -1078,14 +1033,14 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
+      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else if constexpr (LAYOUT_K) {
-      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
+      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else {
       if (!staged)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
+        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, help);
+        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     __syncthreads();

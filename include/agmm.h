@@ -91,14 +91,7 @@ typedef struct agmm_desc {
                             workgroup has work; 0 (default): never split. Measured on the
                             16384x3584x8192 workload the dynamic tile queues already even
                             out most of that round and the split does not pay. */
-  int32_t tile_pieces;   /* fused: fetch pieces (64 rows of a unit) every workgroup claims
-                            and copies at the start of each tile; 0 (default) = none.
-                            Independently of it, a workgroup whose next staged k-group is
-                            not published yet keeps claiming pieces instead of idling. On
-                            the workloads measured, 32 fetchers keep ahead of the GEMM and
-                            pieces at tile start do not pay; they help when few fetchers
-                            are used. */
-  int32_t reserved[1];
+  int32_t reserved[2];
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
@@ -119,7 +112,6 @@ typedef struct agmm_config {
   int32_t split_tiles;          /* tail tiles split along K (the last ones, t_m * T_n + t_n) */
   int32_t split_pieces;         /* pieces per split tile (0 when none is split) */
   int32_t num_items;            /* queue entries: num_tiles + split_tiles * (split_pieces - 1) */
-  int32_t tile_pieces;          /* fetch pieces claimed at each tile start (fused) */
 } agmm_config;
 
 typedef struct agmm_handle agmm_handle;

@@ -20,14 +20,13 @@ bit for bit:
   staged S'  = [t in S if not direct(t)]
   units      = for each window of Wm = max(1, ceil(W / T_n)) consecutive entries of S':
                  for g in 0..G-1: for t in window: (t, g)
-  pieces     = unit u in PPU = BM/64 pieces of 64 rows; piece pc is rows 64*(pc mod PPU)..
-               of unit pc // PPU; pieces are claimed in increasing pc from one counter, by
-               the fetchers and by GEMM workers that help (so a workgroup's pieces ascend)
+  claims     = fetchers take units in increasing u from one counter (so the units of one
+               workgroup ascend); every unit is claimed exactly once
   queues     = GEMM-order m-tiles in super-rows of 4; a super-row's tiles listed in column
                blocks of 8 n-tiles (m-tile, then n, inside a block); super-row j appended
                to queue j mod 8 (one queue per XCD); every tile in exactly one queue
-  flags[t*G + g] == PPU*epoch after a run (each piece adds 1), for every staged unit;
-               direct units untouched
+  flags[t*G + g] == epoch after a run (each run adds 1), for every staged unit; direct
+               units untouched
   staging, k_contiguous:  S[m*K + k] = A[m][k];  m_contiguous: S[k*M + m] = A[m][k]
 """
 from __future__ import annotations
@@ -168,28 +167,12 @@ def fetch_units(g: Geometry) -> List[Tuple[int, int]]:
     return units
 
 
-PIECE_ROWS = 64
-
-
-def pieces_per_unit(g: Geometry) -> int:
-    """Fetch pieces per unit (one for tiles of 64 rows or fewer)."""
-    return max(1, g.BM // PIECE_ROWS)
-
-
-def fetch_pieces(g: Geometry) -> List[Tuple[int, int, int]]:
-    """Piece pc -> (unit index, first row inside the unit, rows), in claim order."""
-    ppu = pieces_per_unit(g)
-    rows = g.BM // ppu
-    return [(pc // ppu, (pc % ppu) * rows, rows) for pc in range(len(fetch_units(g)) * ppu)]
-
-
 def expected_flags(g: Geometry, epoch: int, prior: np.ndarray = None) -> np.ndarray:
-    """Flag array [T_m * G] after a run with the given epoch (flags count published pieces,
-    so after run e a staged unit's flag is PPU * e, modulo 2**32)."""
+    """Flag array [T_m * G] after a run with the given epoch."""
     size = g.T_m * g.G
     flags = np.zeros(size, dtype=np.uint32) if prior is None else prior.astype(np.uint32).copy()
     for (t, kg) in fetch_units(g):
-        flags[t * g.G + kg] = (pieces_per_unit(g) * epoch) % (1 << 32)
+        flags[t * g.G + kg] = epoch
     return flags
 
 

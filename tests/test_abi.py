@@ -72,7 +72,6 @@ def test_validation_errors(A):
     assert _ws(A, D=1, M=8, N=8, K=8, dtype=2) == INV
     assert _ws(A, D=1, M=1 << 23, N=8, K=8) == UNS
     assert _ws(A, D=1, M=8, N=8, K=8, has_bias=2) == INV
-    assert _ws(A, D=1, M=8, N=8, K=8, tile_pieces=-1) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, tail_split=2) == INV
     # create rejects before touching a device
     with pytest.raises(A.AgmmError) as e:

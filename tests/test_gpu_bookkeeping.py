@@ -1,7 +1,7 @@
 """GPU bookkeeping, bit for bit against the schedule model (oracle/schedule_model.py):
 schedule tables, final flag array, staging contents (staging poisoned with NaN first), the
-fetch pieces (each claimed once, in increasing order per workgroup), every output tile
-computed exactly once, every wait seeing its unit complete (pieces per unit x epoch). Also: stale-staging races (alternating inputs, poisoned staging), and the
+fetch units (each claimed once, in increasing order per workgroup), every output tile
+computed exactly once, every wait seeing the run's epoch. Also: stale-staging races (alternating inputs, poisoned staging), and the
 bounded flag wait (a unit whose flag the host never lets the fetcher publish)."""
 import itertools
 
@@ -35,19 +35,15 @@ def geometry(w, cfg):
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("bm", [64, 128])
-@pytest.mark.parametrize("tp", [0, 2])
-def test_bookkeeping_matches_model(w, bm, tp):
-    """tp: fetch pieces every workgroup claims at each tile start (0: only the fetchers and
-    workgroups whose k-group is late fetch)."""
+def test_bookkeeping_matches_model(w, bm):
     import torch
     import all_gather_gemm_amd as A
-    print(f"case {w.name} bm={bm} tp={tp}", flush=True)
+    print(f"case {w.name} bm={bm}", flush=True)
     inp = make_inputs(w)
     g_in = inp.to("cuda")
     op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
                     direct_local=w.direct_local, has_bias=w.has_bias, debug=True, block_m=bm,
-                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096, tail_split=1,
-                    tile_pieces=tp)
+                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096, tail_split=1)
     cfg = op.config.as_dict()
     g = geometry(w, cfg)
     # tables
@@ -79,20 +75,21 @@ def test_bookkeeping_matches_model(w, bm, tp):
         counts, recs = op.trace()
         assert (counts <= cfg["trace_cap"]).all()
         fetched = {wg: [] for wg in range(cfg["num_wgs"])}
-        pieces = sm.fetch_pieces(g)
+        units = sm.fetch_units(g)
         tiles = []
         for wg in range(cfg["num_wgs"]):
             for rec in recs[wg, :counts[wg]]:
                 if rec["event"] == A.EV_FETCH:
-                    pc = int(rec["id"])
-                    fetched[wg].append(pc)
-                    assert (int(rec["a"]), int(rec["b"])) == sm.fetch_units(g)[pieces[pc][0]]
+                    u = int(rec["id"])
+                    fetched[wg].append(u)
+                    assert wg < g.F, "only fetcher workgroups fetch"
+                    assert (int(rec["a"]), int(rec["b"])) == units[u]
                 elif rec["event"] == A.EV_GEMM:
                     tiles.append(int(rec["id"]))
                     tile = int(rec["id"]) & sm.TILE_MASK
                     assert (int(rec["a"]), int(rec["b"])) == sm.gemm_tiles(g)[tile]
                 elif rec["event"] == A.EV_GEMM_WAIT:
-                    assert int(rec["a"]) == sm.pieces_per_unit(g) * epoch
+                    assert int(rec["a"]) == epoch
                     t_m, kg = divmod(int(rec["id"]), g.G)
                     assert not sm.is_direct(g, t_m)
                 else:
@@ -103,8 +100,8 @@ def test_bookkeeping_matches_model(w, bm, tp):
                 posn = {t: i for i, t in enumerate(qlist)}
                 seq = [posn[t] for t in mine if t in posn]
                 assert seq == sorted(seq)
-        # every piece fetched exactly once; a workgroup's claims ascend (one counter)
-        assert sorted(itertools.chain(*fetched.values())) == list(range(len(pieces)))
+        # every unit fetched exactly once; a workgroup's claims ascend (one counter)
+        assert sorted(itertools.chain(*fetched.values())) == list(range(len(units)))
         assert all(v == sorted(v) for v in fetched.values())
         # every queue entry (tile, or piece of a split tile) computed exactly once
         assert sorted(tiles) == sorted(itertools.chain(*sm.tile_queues(g)))

@@ -23,20 +23,16 @@ def test_hand_example_two_shards():
     assert [sm.is_direct(g, t) for t in range(2)] == [True, False]
     assert sm.gemm_tiles(g) == [(0, 0), (0, 1), (1, 0), (1, 1)]
     assert sm.fetch_units(g) == [(1, 0), (1, 1)]
-    assert sm.fetch_pieces(g) == [(0, 0, 2), (1, 0, 2)]
     assert list(sm.expected_flags(g, 7)) == [0, 0, 7, 7]
 
 
-def test_hand_example_pieces_of_a_256_row_tile():
-    # D=2, M=512, BM=256: m-tile 0 is read in place, m-tile 1 is one unit of four 64-row
-    # pieces; after run 3 its flag is 4 * 3
+def test_hand_example_256_row_tile_flags():
+    # D=2, M=512, BM=256: m-tile 0 is read in place, m-tile 1 is one unit; after run 3 its
+    # flag holds 3 and a prior value elsewhere is kept
     g = sm.Geometry(2, 512, 64, 64, 256, 64, 32, 2, 0, True, 1, 4)
     assert sm.fetch_units(g) == [(1, 0)]
-    assert sm.pieces_per_unit(g) == 4
-    assert sm.fetch_pieces(g) == [(0, 0, 64), (0, 64, 64), (0, 128, 64), (0, 192, 64)]
-    assert list(sm.expected_flags(g, 3)) == [0, 12]
-    # flags are 32-bit counters: PPU * epoch wraps modulo 2**32
-    assert list(sm.expected_flags(g, 2**30 + 1)) == [0, 4]
+    assert list(sm.expected_flags(g, 3)) == [0, 3]
+    assert list(sm.expected_flags(g, 4, np.array([9, 3]))) == [9, 4]
 
 
 def test_hand_example_rank_rotation_and_straddle():
@@ -86,20 +82,11 @@ def test_invariants(D, M, N, K, BM, BN, BK, kpf, rank, dl, F, W):
     # rank-rotated shard order among the rest
     keys = [(sm.owner(g, t) - rank) % D for t in order[nd:]]
     assert keys == sorted(keys)
-    # the pieces tile every unit's rows exactly, in unit order
-    ppu = sm.pieces_per_unit(g)
-    pcs = sm.fetch_pieces(g)
-    assert len(pcs) == ppu * len(units)
-    for u in range(len(units)):
-        mine = [(r0, n) for (uu, r0, n) in pcs if uu == u]
-        assert [r0 for r0, _ in mine] == list(range(0, BM, BM // ppu))
-        assert sum(n for _, n in mine) == BM
-    assert [uu for (uu, _, _) in pcs] == sorted(uu for (uu, _, _) in pcs)
     # queues partition the tiles; a split tile appears as its pieces, in the tail queue
     check_queues_partition(g)
-    # flags: exactly the staged units carry PPU * epoch
+    # flags: exactly the staged units carry the epoch
     f = sm.expected_flags(g, 5)
-    assert int((f == 5 * ppu).sum()) == len(units) and int((f == 0).sum()) == f.size - len(units)
+    assert int((f == 5).sum()) == len(units) and int((f == 0).sum()) == f.size - len(units)
     # a k-group is fetched no later than the next k-group of the same m-tile
     pos = {u: i for i, u in enumerate(units)}
     for (t, kg), i in pos.items():
