@@ -65,6 +65,7 @@ class agmm_config(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
         ("split_pieces", ctypes.c_int32), ("num_items", ctypes.c_int32),
+        ("row_wait", ctypes.c_int32),
     ]
 
     def as_dict(self):

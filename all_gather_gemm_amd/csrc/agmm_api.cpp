@@ -226,6 +226,10 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   if (c.num_tiles > 0 && W < 1) W = 1;
   c.num_fetch_wgs = F;
   c.num_wgs = (int32_t)W;
+  // Every unit has a fetcher of its own: the fetch is one pass, so tiles wait for their whole
+  // row at their start and run a K loop without polls (measured faster than per-k-group
+  // waits in that case, and slower when fetchers take several units each).
+  c.row_wait = (n_units > 0 && F >= n_units) ? 1 : 0;
   c.num_copy_wgs = (int32_t)std::min<int64_t>(n_units, 4LL * num_cus);
 
   // Fetch order: staged m-tiles in GEMM order, in windows of the m-tiles the grid works on
@@ -491,6 +495,7 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   if (d.algo == AGMM_ALGO_FUSED) {
     p.F = c.num_fetch_wgs;
     p.staged_kmajor = d.layout == AGMM_K_CONTIGUOUS ? 1 : 0;
+    p.row_wait = c.row_wait;
     AGMM_HIP(agmm::launch_fused(p, d.dtype, c.block_m, c.num_wgs, s));
   } else {
     p.F = 0;

@@ -64,6 +64,7 @@ struct KParams {
   int32_t D, rank, T_m, T_n, G, kpf;
   int32_t num_units, num_tiles, F;
   int32_t staged_kmajor;    // 1: staging is [M][K]; 0: staging is [K][M]
+  int32_t row_wait;         // fused: tiles wait at their start for all of their k-groups
   uint32_t epoch;
   int32_t debug, trace_cap;
   uint32_t spin_limit;

@@ -367,7 +367,7 @@ __device__ inline int grab(const KParams& p);
 // last adds all of them in piece order (so the sum does not depend on which piece ends
 // last) and runs the epilogue. is_last: an LDS word for that decision.
 //
-template <class T, int DT, bool A_KMAJOR, bool WAIT>
+template <class T, int DT, bool A_KMAJOR, bool WAIT, bool ROW>
 __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n,
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
@@ -407,8 +407,9 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   if constexpr (WAIT) {
     if (waits) {
       // every wave requests the first four K-tiles before the K loop's first barrier: wave 0
-      // acquires their k-groups first, this barrier orders the requests after it
-      if (wave0 && KT > 0) acquire_groups((kt_lo + min(KT - 1, 3)) / kpf);
+      // acquires their k-groups first (ROW: all of the tile's k-groups, so the K loop never
+      // waits), this barrier orders the requests after it
+      if (wave0 && KT > 0) acquire_groups(ROW ? g_end - 1 : (kt_lo + min(KT - 1, 3)) / kpf);
       __syncthreads();
       // only wave 0 waits for the rest; the other waves never poll and need no flag state
       waits = wave0 && ready_to < g_end;
@@ -617,14 +618,14 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     for (int r = 0; r < NR; ++r) read_one(r, st.s[0], 0, fa[0], fb[0]);
     int t = 0;
     for (; t + 8 <= KT; t += 4) {
-      wait_range(t + 7);
+      if constexpr (!ROW) wait_range(t + 7);
       step(I0{}, YES{}, t);
       step(I1{}, YES{}, t + 1);
       step(I2{}, YES{}, t + 2);
       step(I3{}, YES{}, t + 3);
     }
     if (t + 4 <= KT) {
-      wait_range(KT - 1);
+      if constexpr (!ROW) wait_range(KT - 1);
       step(I0{}, NO{}, t);
       step(I1{}, NO{}, t + 1);
       step(I2{}, NO{}, t + 2);
@@ -987,8 +988,11 @@ __device__ inline int grab(const KParams& p) {
 }
 
 // FUSED: fetchers + flag waits; LAYOUT_K: staging is k_contiguous (staged and in-place
-// tiles then share one K-major tile routine), else m_contiguous.
-template <int BM, int DT, bool FUSED, bool LAYOUT_K>
+// tiles then share one K-major tile routine), else m_contiguous. ROW (fused): a tile waits
+// at its start for all of its k-groups and its K loop has no waits (used when every fetch
+// unit has a fetcher of its own, so the whole fetch is one pass); otherwise the K loop
+// waits for each k-group as it gets there.
+template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
   __shared__ u32x4 lds0[T::STAGE], lds1[T::STAGE], lds2[T::STAGE], lds3[T::STAGE];
@@ -1033,14 +1037,14 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, false, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else if constexpr (LAYOUT_K) {
-      gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else {
       if (!staged)
-        gemm_tile<T, DT, true, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
       else
-        gemm_tile<T, DT, false, true>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, false, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     __syncthreads();
@@ -1080,17 +1084,22 @@ __global__ void fill32_kernel(uint32_t* dst, int64_t n, uint32_t v) {
     dst[i] = v;
 }
 
-template <int BM, int DT, bool FUSED, bool LAYOUT_K>
+template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW>
 hipError_t launch_t(const KParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((agmm_persistent<BM, DT, FUSED, LAYOUT_K>), dim3(grid), dim3(kThreads), 0, s,
-                     p);
+  hipLaunchKernelGGL((agmm_persistent<BM, DT, FUSED, LAYOUT_K, ROW>), dim3(grid), dim3(kThreads),
+                     0, s, p);
   return hipGetLastError();
 }
 
 template <int BM, bool FUSED, bool LAYOUT_K>
 hipError_t launch_dt(const KParams& p, int dtype, int grid, hipStream_t s) {
-  return dtype == AGMM_BF16 ? launch_t<BM, AGMM_BF16, FUSED, LAYOUT_K>(p, grid, s)
-                            : launch_t<BM, AGMM_F16, FUSED, LAYOUT_K>(p, grid, s);
+  if constexpr (FUSED) {
+    if (p.row_wait)
+      return dtype == AGMM_BF16 ? launch_t<BM, AGMM_BF16, true, LAYOUT_K, true>(p, grid, s)
+                                : launch_t<BM, AGMM_F16, true, LAYOUT_K, true>(p, grid, s);
+  }
+  return dtype == AGMM_BF16 ? launch_t<BM, AGMM_BF16, FUSED, LAYOUT_K, false>(p, grid, s)
+                            : launch_t<BM, AGMM_F16, FUSED, LAYOUT_K, false>(p, grid, s);
 }
 
 // The gemm-only kernel reads k_contiguous staging only.
@@ -1112,17 +1121,22 @@ hipError_t launch_any(const KParams& p, int dtype, int block_m, int grid, hipStr
   }
 }
 
-// The occupancy of the heavier of the two fused variants.
+// The occupancy of the heaviest of the fused variants.
 template <int BM, int DT>
 hipError_t occ_t(int* per_cu) {
-  int a = 0, b = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &a, reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, true>), kThreads, 0);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b, reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, false>), kThreads, 0);
-  *per_cu = a < b ? a : b;
-  return e;
+  const void* ks[4] = {reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, true, false>),
+                       reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, false, false>),
+                       reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, true, true>),
+                       reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, false, true>)};
+  int lo = 1 << 30;
+  for (const void* k : ks) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0);
+    if (e != hipSuccess) return e;
+    lo = n < lo ? n : lo;
+  }
+  *per_cu = lo;
+  return hipSuccess;
 }
 
 }  // namespace

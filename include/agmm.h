@@ -112,6 +112,10 @@ typedef struct agmm_config {
   int32_t split_tiles;          /* tail tiles split along K (the last ones, t_m * T_n + t_n) */
   int32_t split_pieces;         /* pieces per split tile (0 when none is split) */
   int32_t num_items;            /* queue entries: num_tiles + split_tiles * (split_pieces - 1) */
+  int32_t row_wait;             /* fused: 1 when every fetch unit has a fetcher of its own (the
+                                   whole fetch is one pass); a tile then waits at its start for
+                                   all of its k-groups and its K loop never polls. 0: the K loop
+                                   waits for each staged k-group as it reaches it */
 } agmm_config;
 
 typedef struct agmm_handle agmm_handle;

@@ -35,17 +35,24 @@ def geometry(w, cfg):
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 @pytest.mark.parametrize("bm", [64, 128])
-def test_bookkeeping_matches_model(w, bm):
+@pytest.mark.parametrize("kpf,nf", [(2, 5), (32, 64)], ids=["kloop_waits", "row_waits"])
+def test_bookkeeping_matches_model(w, bm, kpf, nf):
+    """(2, 5): fetchers take many units each and the K loop waits per k-group; (32, 64): every
+    unit has a fetcher of its own and tiles wait for their whole row at their start."""
     import torch
     import all_gather_gemm_amd as A
-    print(f"case {w.name} bm={bm}", flush=True)
+    print(f"case {w.name} bm={bm} kpf={kpf} fetchers={nf}", flush=True)
     inp = make_inputs(w)
     g_in = inp.to("cuda")
     op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
                     direct_local=w.direct_local, has_bias=w.has_bias, debug=True, block_m=bm,
-                    k_per_flag=2, num_fetch_wgs=5, trace_cap=4096, tail_split=1)
+                    k_per_flag=kpf, num_fetch_wgs=nf, trace_cap=4096, tail_split=1)
     cfg = op.config.as_dict()
     g = geometry(w, cfg)
+    n_units = len(sm.fetch_units(g))
+    assert cfg["row_wait"] == int(n_units > 0 and cfg["num_fetch_wgs"] >= n_units)
+    if kpf == 32 and n_units:
+        assert cfg["row_wait"] == 1
     # tables
     assert [tuple(u) for u in op.units()] == sm.fetch_units(g)
     assert op.queues() == sm.tile_queues(g)
