@@ -382,10 +382,6 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   bool waits = WAIT && staged;
   const int kpf = p.kpf;
   const uint32_t target = p.epoch;  // a published unit's flag
-  auto flag_of = [&](int g) {
-    return uniform32(__hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
-  };
   // Consumer side of the flags. An agent-scope acquire invalidates the XCD's L2 (which all
   // workgroups on that XCD rely on for operand reuse) and drains the wave's DMA requests in
   // flight, so acquires are few: only wave 0 polls and acquires, and each acquire also
@@ -396,11 +392,27 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   const bool wave0 = __builtin_amdgcn_readfirstlane(tid_in >> 6) == 0;
   const int g_end = (kt_lo + KT + kpf - 1) / kpf;  // one past this piece's last k-group
   int ready_to = kt_lo / kpf;
+  // First k-group at or after g0 whose flag is not published yet (g_end if none). The
+  // flags are read up to 64 at a time, one per lane, so a run of published k-groups costs
+  // one memory round trip rather than one per group.
+  auto unpublished_from = [&](int g0) -> int {
+    for (int base = g0; base < g_end; base += 64) {
+      const int g = base + (tid_in & 63);
+      uint32_t v = target;
+      if (g < g_end)
+        v = __hip_atomic_load(p.flags + fbase + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t late = __builtin_amdgcn_ballot_w64(v != target);
+      if (late) return base + (int)__builtin_ctzll(late);
+    }
+    return g_end;
+  };
   // wave 0: wait for k-groups ready_to .. g_need, take the published ones after them, acquire
   auto acquire_groups = [&](int g_need) {
-    for (int g = ready_to; g <= g_need; ++g) poll_flag(p, fbase + g, target, tr);
-    int g = g_need + 1;
-    while (g < g_end && flag_of(g) == target) ++g;
+    int g = unpublished_from(ready_to);
+    while (g <= g_need) {  // a needed k-group is not published yet: wait for it
+      poll_flag(p, fbase + g, target, tr);
+      g = unpublished_from(g + 1);
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     ready_to = g;
   };
@@ -696,6 +708,13 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     constexpr bool SPLIT = decltype(split_tag)::value;
     const rsrc_t prs = make_rsrc(reinterpret_cast<const uint16_t*>(parts),
                                  SPLIT ? (int64_t)pieces * BM * BN * 4 : 0);
+    // this lane's bias pairs, read from LDS in one batch (one wait instead of one per group)
+    u32x2 bias_r[T::FN][4];
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bias_r[fn][g] = bias_lds[(wn * T::WTN + fn * 32 + g * 8 + (lane >> 5) * 4) >> 2];
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm) {
       const int ml = wm * T::WTM + fm * 32 + (lane & 31);
@@ -734,7 +753,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
             }
             x0 = y0, x1 = y1, x2 = y2, x3 = y3;
           }
-          const u32x2 bb = bias_lds[nl >> 2];
+          const u32x2 bb = bias_r[fn][g];
           x0 += Num<DT>::from_bits(bb[0] & 0xffffu);
           x1 += Num<DT>::from_bits(bb[0] >> 16);
           x2 += Num<DT>::from_bits(bb[1] & 0xffffu);
@@ -753,15 +772,27 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   else
     to_lds(std::false_type{});
   __syncthreads();
+  // The tile to global memory: each thread's chunks c = tid + i * kThreads, read from LDS
+  // in batches of CB before their stores; chunks outside the output (ragged tiles) go to an
+  // out-of-range offset, so the stores need no branch.
   constexpr int ROW_C = BN / 8;  // 16-byte chunks per row
-#pragma unroll 4
-  for (int c = tid; c < BM * ROW_C; c += kThreads) {
-    const int r = c / ROW_C, ch = c % ROW_C;
-    const int s = r & XM;
-    u32x4 v = *reinterpret_cast<const u32x4*>(unit_ptr(r, ((2 * ch) ^ s) & ~1));
-    if (s & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-    if (r < rows_valid && ch * 8 < cols_valid)
-      *reinterpret_cast<u32x4*>(p.out + (m0 + r) * p.N + n0 + ch * 8) = v;
+  constexpr int CPT = BM * ROW_C / kThreads, CB = CPT < 8 ? CPT : 8;
+  static_assert(CPT % CB == 0, "chunk batches");
+  const rsrc_t ors = make_rsrc(p.out + m0 * p.N + n0, (p.M - m0) * p.N * 2 - n0 * 2);
+#pragma unroll
+  for (int i0 = 0; i0 < CPT; i0 += CB) {
+    u32x4 v[CB];
+    uint32_t off[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = tid + (i0 + j) * kThreads, r = c / ROW_C, ch = c % ROW_C;
+      const int sw = r & XM;
+      v[j] = *reinterpret_cast<const u32x4*>(unit_ptr(r, ((2 * ch) ^ sw) & ~1));
+      if (sw & 1) v[j] = u32x4{v[j][2], v[j][3], v[j][0], v[j][1]};
+      off[j] = (r < rows_valid && ch * 8 < cols_valid) ? (uint32_t)((r * p.N + ch * 8) * 2) : kOob;
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bstore16(ors, off[j], v[j]);
   }
   __syncthreads();  // the tile area is the next tile's stages
 }
