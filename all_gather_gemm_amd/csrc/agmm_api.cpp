@@ -232,20 +232,44 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   c.row_wait = (n_units > 0 && F >= n_units) ? 1 : 0;
   c.num_copy_wgs = (int32_t)std::min<int64_t>(n_units, 4LL * num_cus);
 
-  // Fetch order: staged m-tiles in GEMM order, in windows of the m-tiles the grid works on
-  // at once; inside a window, k-group by k-group.
+  make_queues(T_m, T_n, pl->mtiles, S, pl);
+
+  // Fetch order follows the order in which the tile queues reach the m-tiles, modelled as
+  // the W workgroups draining the 8 per-XCD queues evenly (stealing included): entry i of
+  // queue x is the k-th in the order (i, x) over existing entries, reached in round k / W.
+  // An m-tile's window is the first round that reaches one of its tiles (tail-queue pieces
+  // count as after every round). Staged m-tiles are fetched window by window, in GEMM order
+  // inside a window, and inside a window k-group by k-group, so the first k-groups of every
+  // m-tile a round starts on come first.
+  std::vector<int64_t> first_round(T_m, INT64_MAX);
+  int32_t longest = 0;
+  for (int x = 0; x < agmm::kQueues; ++x) longest = std::max(longest, pl->qlen[x]);
+  for (int64_t i = 0, k = 0; i < longest; ++i)
+    for (int x = 0; x < agmm::kQueues; ++x) {
+      if (i >= pl->qlen[x]) continue;
+      const uint32_t q = pl->qtiles[pl->qoff[x] + i] & agmm::kItemTileMask;
+      const int64_t pos = (int64_t)q / T_n;
+      first_round[pos] = std::min<int64_t>(first_round[pos], k / std::max<int64_t>(1, W));
+      ++k;
+    }
+  std::vector<std::pair<int64_t, int64_t>> staged_pos;  // (window, GEMM position)
+  for (int64_t pos = 0; pos < T_m; ++pos)
+    if (!(pl->mtiles[pos] >> 31)) staged_pos.push_back({first_round[pos], pos});
+  std::stable_sort(staged_pos.begin(), staged_pos.end(),
+                   [](const std::pair<int64_t, int64_t>& a, const std::pair<int64_t, int64_t>& b) {
+                     return a.first < b.first;
+                   });
   pl->units.clear();
-  const int64_t wm = std::max<int64_t>(1, cdiv(W, std::max<int64_t>(1, T_n)));
-  for (size_t ws = 0; ws < other.size(); ws += (size_t)wm) {
-    const size_t we = std::min(other.size(), ws + (size_t)wm);
+  for (size_t ws = 0; ws < staged_pos.size();) {
+    size_t we = ws;
+    while (we < staged_pos.size() && staged_pos[we].first == staged_pos[ws].first) ++we;
     for (int64_t g = 0; g < G; ++g)
       for (size_t i = ws; i < we; ++i) {
-        pl->units.push_back((uint32_t)other[i]);
+        pl->units.push_back(pl->mtiles[staged_pos[i].second] & 0x7fffffffu);
         pl->units.push_back((uint32_t)g);
       }
+    ws = we;
   }
-
-  make_queues(T_m, T_n, pl->mtiles, S, pl);
 
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
   pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;

@@ -18,8 +18,9 @@ bit for bit:
   S          = direct m-tiles ascending, then the others by ((owner - rank) mod D, t)
   tile q     = (S[q // T_n], q % T_n)                GEMM order, n fastest
   staged S'  = [t in S if not direct(t)]
-  units      = for each window of Wm = max(1, ceil(W / T_n)) consecutive entries of S':
-                 for g in 0..G-1: for t in window: (t, g)
+  units      = staged m-tiles grouped by the round in which the queues first reach them
+               (entries in (i, x) order, the k-th in round k // W); window by window, GEMM
+               order inside a window: for g in 0..G-1: for t in window: (t, g)
   claims     = fetchers take units in increasing u from one counter (so the units of one
                workgroup ascend); every unit is claimed exactly once
   queues     = GEMM-order m-tiles in super-rows of 4; a super-row's tiles listed in column
@@ -155,15 +156,31 @@ def tile_queues(g: Geometry) -> List[List[int]]:
 
 
 def fetch_units(g: Geometry) -> List[Tuple[int, int]]:
-    """Unit u -> (t_m, k-group) in fetch order."""
-    staged = [t for t in mtile_order(g) if not is_direct(g, t)]
-    wm = max(1, -(-g.W // max(1, g.T_n)))
+    """Unit u -> (t_m, k-group) in fetch order.
+
+    The W workgroups are taken to drain the 8 per-XCD queues evenly: list the entries in the
+    order (i, x) (entry i of queue x, only those that exist); the k-th is reached in round
+    k // W. An m-tile's window is the earliest round over its entries (an m-tile whose tiles
+    are all split pieces comes after every round). Staged m-tiles go window by window, in
+    GEMM order inside a window, and a window is fetched k-group by k-group."""
+    order = mtile_order(g)
+    queues = tile_queues(g)[:N_QUEUES]
+    first = [float("inf")] * g.T_m
+    interleaved = sorted((i, x) for x in range(N_QUEUES) for i in range(len(queues[x])))
+    for k, (i, x) in enumerate(interleaved):
+        pos = (queues[x][i] & TILE_MASK) // g.T_n
+        first[pos] = min(first[pos], k // max(1, g.W))
+    staged = sorted((first[pos], pos) for pos in range(g.T_m) if not is_direct(g, order[pos]))
     units = []
-    for ws in range(0, len(staged), wm):
-        win = staged[ws:ws + wm]
+    i = 0
+    while i < len(staged):
+        j = i
+        while j < len(staged) and staged[j][0] == staged[i][0]:
+            j += 1
         for kg in range(g.G):
-            for t in win:
-                units.append((t, kg))
+            for _, pos in staged[i:j]:
+                units.append((order[pos], kg))
+        i = j
     return units
 
 

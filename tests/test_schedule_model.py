@@ -53,6 +53,22 @@ def test_hand_example_four_shards_rank2():
     assert sm.fetch_units(g) == [(3, 0), (0, 0), (1, 0)]   # window of 2: [3, 0], then [1]
 
 
+def test_hand_example_fetch_windows_follow_the_queues():
+    # 12 m-tiles, one column, all staged: super-rows of 4 go to queues 0, 1, 2. With W = 4
+    # workgroups draining the queues evenly, the entries in (i, x) order are m-tiles
+    # 0, 4, 8, 1 | 5, 9, 2, 6 | 10, 3, 7, 11, four per round. An m-tile's window is its round;
+    # inside a window the order is GEMM order (here the m-tile index).
+    g = sm.Geometry(D=2, M=24, N=1, K=2, BM=2, BN=1, BK=1, k_per_flag=2, rank=0,
+                    direct_local=False, F=2, W=4)
+    assert sm.mtile_order(g) == list(range(12))
+    assert sm.tile_queues(g)[:3] == [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11]]
+    assert sm.fetch_units(g) == [(t, 0) for t in (0, 1, 4, 8, 2, 5, 6, 9, 3, 7, 10, 11)]
+    # two k-groups: a window is fetched k-group by k-group
+    g2 = sm.Geometry(D=2, M=24, N=1, K=4, BM=2, BN=1, BK=1, k_per_flag=2, rank=0,
+                     direct_local=False, F=2, W=4)
+    assert sm.fetch_units(g2)[:8] == [(0, 0), (1, 0), (4, 0), (8, 0), (0, 1), (1, 1), (4, 1), (8, 1)]
+
+
 def test_direct_local_off_stages_everything():
     g = geo(direct_local=False)
     assert sorted(sm.fetch_units(g)) == [(0, 0), (0, 1), (1, 0), (1, 1)]
