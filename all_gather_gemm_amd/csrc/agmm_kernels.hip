@@ -150,6 +150,13 @@ __device__ inline void bstore16(rsrc_t rs, uint32_t off, u32x4 v) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// LDS pointers kept in the LDS address space, so that every access through them is a ds_*
+// instruction (a generic pointer makes the compiler emit flat accesses, which are slower
+// and count against both the vector-memory and the LDS wait counters)
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const char lds_cchar;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // 16 bytes per lane from rs at voff into LDS at byte address m0 + 16 * lane (m0 is
 // wave-uniform): buffer_load_dwordx4 ... lds, with the LDS base in M0. Written as inline
@@ -186,7 +193,7 @@ struct KMajorDma {
   }
   // MFMA operand for rows rbase..rbase+31, K sub-step kk: lane l holds row rbase + l%32,
   // K values 16*kk + 8*(l/32) .. +7.
-  __device__ static inline u32x4 frag(const u32x4* region, int rbase, int kk, int lane) {
+  __device__ static inline u32x4 frag(const lds_u32x4* region, int rbase, int kk, int lane) {
     const int row = rbase + (lane & 31), c = 2 * kk + (lane >> 5);
     return region[row * 4 + (c ^ g_row(row))];
   }
@@ -222,8 +229,8 @@ struct MNMajorDma {
     const int mn = mbase + 16 * (gidx & 1) + 4 * (s & 3);
     return kl * ROWB + (((mn >> 3) ^ f_row<RC>(kl)) * 16) + (mn & 7) * 2;
   }
-  __device__ static inline u32x4 frag(const u32x4* region, int off, int kk) {
-    const char* p = reinterpret_cast<const char*>(region) + off + 16 * kk * ROWB;
+  __device__ static inline u32x4 frag(const lds_u32x4* region, int off, int kk) {
+    lds_cchar* p = reinterpret_cast<lds_cchar*>(region) + off + 16 * kk * ROWB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -336,7 +343,7 @@ __device__ inline void kloop_barrier() {
 // filled by DMA from the stage being read; off[] are their LDS byte addresses (uniform).
 template <class T>
 struct Stages {
-  u32x4* s[4];
+  lds_u32x4* s[4];
   uint32_t off[4];
 };
 
@@ -526,7 +533,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     for (int d = 0; d < T::DMA_PER_TILE; ++d) issue(d, r, stage_off);
   };
   // Fragment read number i of a half step: A operands first, then B.
-  auto read_one = [&](int i, const u32x4* stage, int kk, u32x4 (&a)[T::FM], u32x4 (&b)[T::FN]) {
+  auto read_one = [&](int i, const lds_u32x4* stage, int kk, u32x4 (&a)[T::FM], u32x4 (&b)[T::FN]) {
     if (i < T::FM) {
       if constexpr (A_KMAJOR)
         a[i] = KMajorDma<BM>::frag(stage, wm * T::WTM + i * 32, kk, lane);
@@ -548,8 +555,8 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   auto step = [&](auto s_tag, auto full_tag, int t) {
     constexpr int S = decltype(s_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
-    const u32x4* cur = st.s[S];
-    const u32x4* nxt = st.s[(S + 1) & 3];
+    const lds_u32x4* cur = st.s[S];
+    const lds_u32x4* nxt = st.s[(S + 1) & 3];
     // part 1: sub-step 0 MFMAs of t; sub-step 1 fragments of t and the B slice of t + 3
     // (into the stage of t - 1, free since the last barrier) in between
     const bool do_req1 = FULL || t + 3 < KT;
@@ -698,8 +705,8 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   constexpr int ROW_U = BN / 4;  // 8-byte units per tile row
   constexpr int XM = (ROW_U < 32 ? ROW_U : 32) - 1;
   constexpr int QR = BM / 4;     // rows per quarter
-  auto unit_ptr = [&](int r, int u) -> uint32_t* {
-    return reinterpret_cast<uint32_t*>(st.s[r / QR]) + ((r % QR) * ROW_U + u) * 2;
+  auto unit_ptr = [&](int r, int u) -> lds_u32* {
+    return reinterpret_cast<lds_u32*>(st.s[r / QR]) + ((r % QR) * ROW_U + u) * 2;
   };
   // The accumulators to LDS; SPLIT: plus the other pieces' partial sums, added in piece
   // order (reads past the last piece are out of the slots' range and return zeros, so
@@ -761,7 +768,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
           u32x2 o;
           o[0] = Num<DT>::to_bits(x0) | (Num<DT>::to_bits(x1) << 16);
           o[1] = Num<DT>::to_bits(x2) | (Num<DT>::to_bits(x3) << 16);
-          *reinterpret_cast<u32x2*>(unit_ptr(ml, (nl >> 2) ^ (ml & XM))) = o;
+          *reinterpret_cast<lds_u32x2*>(unit_ptr(ml, (nl >> 2) ^ (ml & XM))) = o;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -787,7 +794,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     for (int j = 0; j < CB; ++j) {
       const int c = tid + (i0 + j) * kThreads, r = c / ROW_C, ch = c % ROW_C;
       const int sw = r & XM;
-      v[j] = *reinterpret_cast<const u32x4*>(unit_ptr(r, ((2 * ch) ^ sw) & ~1));
+      v[j] = *reinterpret_cast<const lds_u32x4*>(unit_ptr(r, ((2 * ch) ^ sw) & ~1));
       if (sw & 1) v[j] = u32x4{v[j][2], v[j][3], v[j][0], v[j][1]};
       off[j] = (r < rows_valid && ch * 8 < cols_valid) ? (uint32_t)((r * p.N + ch * 8) * 2) : kOob;
     }
@@ -1029,10 +1036,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   __shared__ u32x4 lds0[T::STAGE], lds1[T::STAGE], lds2[T::STAGE], lds3[T::STAGE];
   __shared__ u32x2 s_bias[T::BN / 4];
   Stages<T> st;
-  st.s[0] = lds0;
-  st.s[1] = lds1;
-  st.s[2] = lds2;
-  st.s[3] = lds3;
+  st.s[0] = (lds_u32x4*)lds0;
+  st.s[1] = (lds_u32x4*)lds1;
+  st.s[2] = (lds_u32x4*)lds2;
+  st.s[3] = (lds_u32x4*)lds3;
   st.off[0] = (uint32_t)(size_t)(lds_void*)lds0;
   st.off[1] = (uint32_t)(size_t)(lds_void*)lds1;
   st.off[2] = (uint32_t)(size_t)(lds_void*)lds2;
