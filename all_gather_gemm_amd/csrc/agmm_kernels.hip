@@ -705,8 +705,10 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   constexpr int ROW_U = BN / 4;  // 8-byte units per tile row
   constexpr int XM = (ROW_U < 32 ? ROW_U : 32) - 1;
   constexpr int QR = BM / 4;     // rows per quarter
+  // (stages are contiguous: quarter q starts q stages after stage 0)
   auto unit_ptr = [&](int r, int u) -> lds_u32* {
-    return reinterpret_cast<lds_u32*>(st.s[r / QR]) + ((r % QR) * ROW_U + u) * 2;
+    return reinterpret_cast<lds_u32*>(st.s[0]) + (r / QR) * (T::STAGE * 4) +
+           ((r % QR) * ROW_U + u) * 2;
   };
   // The accumulators to LDS; SPLIT: plus the other pieces' partial sums, added in piece
   // order (reads past the last piece are out of the slots' range and return zeros, so
@@ -1033,17 +1035,17 @@ __device__ inline int grab(const KParams& p) {
 template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
-  __shared__ u32x4 lds0[T::STAGE], lds1[T::STAGE], lds2[T::STAGE], lds3[T::STAGE];
+  // the four stages, contiguous: a stage's base is then arithmetic on the first one's
+  // address, also where the stage index is only known at run time (the epilogue)
+  __shared__ u32x4 lds_stages[4 * T::STAGE];
   __shared__ u32x2 s_bias[T::BN / 4];
   Stages<T> st;
-  st.s[0] = (lds_u32x4*)lds0;
-  st.s[1] = (lds_u32x4*)lds1;
-  st.s[2] = (lds_u32x4*)lds2;
-  st.s[3] = (lds_u32x4*)lds3;
-  st.off[0] = (uint32_t)(size_t)(lds_void*)lds0;
-  st.off[1] = (uint32_t)(size_t)(lds_void*)lds1;
-  st.off[2] = (uint32_t)(size_t)(lds_void*)lds2;
-  st.off[3] = (uint32_t)(size_t)(lds_void*)lds3;
+  const uint32_t lds_base = (uint32_t)(size_t)(lds_void*)lds_stages;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.s[i] = (lds_u32x4*)lds_stages + i * T::STAGE;
+    st.off[i] = lds_base + (uint32_t)(i * T::STAGE * 16);
+  }
   __shared__ int s_next, s_last, s_claim;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
