@@ -74,7 +74,7 @@ struct Num<AGMM_BF16> {
   }
 };
 
-// Tile family: square BMxBM output tile (BM = 256, 128, 64), BK = 32, four LDS stages.
+// Tile family: square BMxBM output tile (BM = 256, 128, 64), BK = 32, NS LDS stages.
 // A stage holds the A and B slices of one K-tile, 4*BM 16-byte chunks each, in the layout
 // their source has in global memory, so both are copied global->LDS by buffer loads that
 // write LDS directly (no registers, no VALU):
@@ -97,7 +97,14 @@ struct Tile {
   static constexpr int DMA_PER_TILE = ADMA + BDMA;
   static constexpr int WTM = BM / 2, WTN = BN / 2;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
+  // LDS stages, i.e. K-tiles in flight + 1. Four at every tile size: deeper pipelines for
+  // the small tiles (8 or 16 stages at BM = 64, the same 128 KiB as BM = 256) measured
+  // slower, the extra requests only lengthen the memory queues.
+  static constexpr int NS = 4;
+  static_assert(NS >= 4 && NS * STAGE <= 8192, "stages fit in 128 KiB");
   static_assert(STAGE * 16 >= (BM / 4) * BN * 2, "an output quarter fits in a stage");
+  // requests in flight per wave: at most NS - 2 K-tiles and one A slice (counter range 63)
+  static_assert((NS - 2) * DMA_PER_TILE + ADMA <= 63, "DMA requests within the counter");
 };
 
 __device__ inline int g_row(int m) { return ((m >> 1) ^ (m >> 3)) & 3; }
@@ -339,13 +346,38 @@ __device__ inline void kloop_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The four LDS stages, each its own array so that the compiler can tell a stage being
-// filled by DMA from the stage being read; off[] are their LDS byte addresses (uniform).
+// The NS LDS stages, contiguous: stage i and its LDS byte address (uniform) are arithmetic
+// on stage 0's, so they cost no registers and need no table.
 template <class T>
 struct Stages {
-  lds_u32x4* s[4];
-  uint32_t off[4];
+  lds_u32x4* base;
+  uint32_t off0;
+  __device__ inline lds_u32x4* s(int i) const { return base + i * T::STAGE; }
+  __device__ inline uint32_t off(int i) const { return off0 + (uint32_t)(i * T::STAGE * 16); }
 };
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1, in order.
+template <int I, int N, class Fn>
+__device__ __attribute__((always_inline)) inline void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// s_waitcnt vmcnt(a * PER), a <= A_MAX a run-time value: the largest allowed count not above
+// it (a chain of uniform compares; the count has to be an immediate).
+template <int PER, int A_MAX>
+__device__ inline void wait_vmcnt_times(int a) {
+  if constexpr (A_MAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (a >= A_MAX)
+      wait_vmcnt<A_MAX * PER>();
+    else
+      wait_vmcnt_times<PER, A_MAX - 1>(a);
+  }
+}
 
 // Issue slot of item i of n spread over the m MFMAs of a half step: item i goes after MFMA
 // slot(i) (shift 0) or half a spacing later (shift 1), so that DMA requests and fragment
@@ -425,10 +457,11 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   };
   if constexpr (WAIT) {
     if (waits) {
-      // every wave requests the first four K-tiles before the K loop's first barrier: wave 0
+      // every wave requests the first NS K-tiles before the K loop's first barrier: wave 0
       // acquires their k-groups first (ROW: all of the tile's k-groups, so the K loop never
       // waits), this barrier orders the requests after it
-      if (wave0 && KT > 0) acquire_groups(ROW ? g_end - 1 : (kt_lo + min(KT - 1, 3)) / kpf);
+      if (wave0 && KT > 0)
+        acquire_groups(ROW ? g_end - 1 : (kt_lo + min(KT - 1, T::NS - 1)) / kpf);
       __syncthreads();
       // only wave 0 waits for the rest; the other waves never poll and need no flag state
       waits = wave0 && ready_to < g_end;
@@ -507,7 +540,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     int64_t k_rem;
   };
   // Fused mode: make the staged k-groups of K-tiles up to hi (of this piece) available.
-  // Called once per block of four K-tiles, before the block that requests them (their
+  // Called once per block of NS K-tiles, before the block that requests them (their
   // requests follow a K-loop barrier), so the polling stays outside the MFMA stream; only
   // wave 0 acts, and only when the block reaches a k-group it has not acquired yet.
   auto wait_range = [&](int hi) {
@@ -547,20 +580,21 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
 
   u32x4 fa[2][T::FM], fb[2][T::FN];
 
-  // One K-tile step with compile-time stage index S (= t % 4). FULL: t + 4 < KT, so every
+  // One K-tile step with compile-time stage index S (= t % NS). FULL: t + NS < KT, so every
   // request below exists. The DMA of a K-tile is issued in two halves one step apart: its
-  // A slice in part 2 of step t - 4 (the step that frees the stage), its B slice in part 1
-  // of step t - 3, so the texture path and the LDS see a steady stream of requests over
-  // the whole step instead of a burst after each barrier.
-  auto step = [&](auto s_tag, auto full_tag, int t) {
+  // A slice in part 2 of step t - NS (the step that frees the stage), its B slice in part 1
+  // of step t - NS + 1, so the texture path and the LDS see a steady stream of requests
+  // over the whole step instead of a burst after each barrier.
+  constexpr int NS = T::NS;
+  auto step = [&](auto s_tag, auto full_tag, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(s_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
-    const lds_u32x4* cur = st.s[S];
-    const lds_u32x4* nxt = st.s[(S + 1) & 3];
-    // part 1: sub-step 0 MFMAs of t; sub-step 1 fragments of t and the B slice of t + 3
-    // (into the stage of t - 1, free since the last barrier) in between
-    const bool do_req1 = FULL || t + 3 < KT;
-    const Req rq1 = resources(t + 3);  // plain arithmetic, also past the last K-tile
+    const lds_u32x4* cur = st.s(S);
+    const lds_u32x4* nxt = st.s((S + 1) % NS);
+    // part 1: sub-step 0 MFMAs of t; sub-step 1 fragments of t and the B slice of
+    // t + NS - 1 (into the stage of t - 1, free since the last barrier) in between
+    const bool do_req1 = FULL || t + NS - 1 < KT;
+    const Req rq1 = resources(t + NS - 1);  // plain arithmetic, also past the last K-tile
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int fm = i / T::FN, fn = i % T::FN;
@@ -571,25 +605,23 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
       if (do_req1) {
 #pragma unroll
         for (int d = 0; d < T::BDMA; ++d)
-          if (spread(d, T::BDMA, NM, 1) == i) issue(T::ADMA + d, rq1, st.off[(S + 3) & 3]);
+          if (spread(d, T::BDMA, NM, 1) == i)
+            issue(T::ADMA + d, rq1, st.off((S + NS - 1) % NS));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // requests issued after the last one of t + 1, which this wave may leave in flight:
-    // those of t + 2 and t + 3 that exist
-    const int ahead = FULL ? 2 : min(KT - 1, t + 3) - (t + 1);
-    if (ahead >= 2)
-      wait_vmcnt<2 * ND>();
-    else if (ahead == 1)
-      wait_vmcnt<ND>();
+    // those of t + 2 .. t + NS - 1 that exist
+    if constexpr (FULL)
+      wait_vmcnt<(NS - 2) * ND>();
     else
-      wait_vmcnt<0>();
+      wait_vmcnt_times<ND, NS - 2>(min(KT - 1, t + NS - 1) - (t + 1));
     kloop_barrier();
-    // part 2: sub-step 1 MFMAs of t; the A slice of t + 4 into stage S and sub-step 0
+    // part 2: sub-step 1 MFMAs of t; the A slice of t + NS into stage S and sub-step 0
     // fragments of t + 1 in between
-    const bool do_req = FULL || t + 4 < KT;
+    const bool do_req = FULL || t + NS < KT;
     const bool do_read = FULL || t + 1 < KT;
-    const Req rq = resources(t + 4);
+    const Req rq = resources(t + NS);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int fm = i / T::FN, fn = i % T::FN;
@@ -597,7 +629,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
       if (do_req) {
 #pragma unroll
         for (int d = 0; d < T::ADMA; ++d)
-          if (spread(d, T::ADMA, NM, 0) == i) issue(d, rq, st.off[S]);
+          if (spread(d, T::ADMA, NM, 0) == i) issue(d, rq, st.off(S));
       }
       if (do_read) {
 #pragma unroll
@@ -607,53 +639,40 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
   using YES = std::true_type;
   using NO = std::false_type;
 
   if (KT > 0) {
-    request(0, st.off[0]);  // k-groups of K-tiles 0..3 acquired before the tile's barrier
-    if (KT > 1) request(1, st.off[1]);
-    if (KT > 2) request(2, st.off[2]);
-    if (KT > 3) {  // the A slice only: step 0 requests the B slice
-      const Req r = resources(3);
+    // K-tiles 0 .. NS - 2 and the A slice of NS - 1 (k-groups acquired before the tile's
+    // barrier); step 0 requests the B slice of NS - 1
+    static_for<0, NS - 1>([&](auto j) __attribute__((always_inline)) {
+      if (j < KT) request(j, st.off(j));
+    });
+    if (KT > NS - 1) {
+      const Req r = resources(NS - 1);
 #pragma unroll
-      for (int d = 0; d < T::ADMA; ++d) issue(d, r, st.off[3]);
+      for (int d = 0; d < T::ADMA; ++d) issue(d, r, st.off(NS - 1));
     }
-    const int ahead0 = min(KT - 1, 3);
-    if (ahead0 >= 3)
-      wait_vmcnt<2 * ND + T::ADMA>();
-    else if (ahead0 == 2)
-      wait_vmcnt<2 * ND>();
-    else if (ahead0 == 1)
-      wait_vmcnt<ND>();
+    // requests after the last one of K-tile 0
+    if (KT - 1 >= NS - 1)
+      wait_vmcnt<(NS - 2) * ND + T::ADMA>();
     else
-      wait_vmcnt<0>();
+      wait_vmcnt_times<ND, NS - 2>(KT - 1);
     kloop_barrier();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(r, st.s[0], 0, fa[0], fb[0]);
+    for (int r = 0; r < NR; ++r) read_one(r, st.s(0), 0, fa[0], fb[0]);
     int t = 0;
-    for (; t + 8 <= KT; t += 4) {
-      if constexpr (!ROW) wait_range(t + 7);
-      step(I0{}, YES{}, t);
-      step(I1{}, YES{}, t + 1);
-      step(I2{}, YES{}, t + 2);
-      step(I3{}, YES{}, t + 3);
+    for (; t + 2 * NS <= KT; t += NS) {
+      if constexpr (!ROW) wait_range(t + 2 * NS - 1);
+      static_for<0, NS>([&](auto j) __attribute__((always_inline)) { step(j, YES{}, t + j); });
     }
-    if (t + 4 <= KT) {
-      if constexpr (!ROW) wait_range(KT - 1);
-      step(I0{}, NO{}, t);
-      step(I1{}, NO{}, t + 1);
-      step(I2{}, NO{}, t + 2);
-      step(I3{}, NO{}, t + 3);
-      t += 4;
+    // the last NS .. 2 NS - 1 K-tiles (fewer when KT < 2 NS): at most two passes
+    if constexpr (!ROW) wait_range(KT - 1);
+    for (; t < KT; t += NS) {
+      static_for<0, NS>([&](auto j) __attribute__((always_inline)) {
+        if (t + j < KT) step(j, NO{}, t + j);
+      });
     }
-    if (t < KT) step(I0{}, NO{}, t);
-    if (t + 1 < KT) step(I1{}, NO{}, t + 1);
-    if (t + 2 < KT) step(I2{}, NO{}, t + 2);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (tid == 0) *next_tile = grab(p);
@@ -707,7 +726,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   constexpr int QR = BM / 4;     // rows per quarter
   // (stages are contiguous: quarter q starts q stages after stage 0)
   auto unit_ptr = [&](int r, int u) -> lds_u32* {
-    return reinterpret_cast<lds_u32*>(st.s[0]) + (r / QR) * (T::STAGE * 4) +
+    return reinterpret_cast<lds_u32*>(st.s(0)) + (r / QR) * (T::STAGE * 4) +
            ((r % QR) * ROW_U + u) * 2;
   };
   // The accumulators to LDS; SPLIT: plus the other pieces' partial sums, added in piece
@@ -819,9 +838,13 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
   __syncthreads();
 }
 
-// A fetcher workgroup keeps 128 KiB of loads in flight (32 x 16 bytes per thread): one
-// workgroup's copy rate is bound by latency, not by its share of the HBM bandwidth.
-constexpr int kFetchDepth = 32;
+// A fetcher workgroup's copy rate is bound by latency, not by its share of the HBM
+// bandwidth, so the copies run as a two-batch software pipeline: the loads of batch n + 1
+// are issued before the stores of batch n, so neither waits for the other (a wait for
+// loads also waits for every store issued before them: the vector memory counter retires
+// in order). A batch is kCopyBatch 16-byte loads per thread (64 KiB per workgroup); at
+// most three batches of requests are in flight, within the counter's range of 63.
+constexpr int kCopyBatch = 16;
 
 // Source row pointers of one unit: rows m_beg .. m_beg + R - 1 of the gathered A. A unit
 // inside one shard (the usual case) needs no per-row shard lookup.
@@ -843,8 +866,8 @@ struct UnitRows {
 // c = r * CR + cc of the unit goes to thread c % 256; the (r, cc) of successive chunks of a
 // thread advance by fixed steps, so the loop does no division. When the unit lies in one
 // shard (the usual case) the loads and stores are range-checked buffer accesses: a lane
-// past the unit reads zero and its store is dropped, so the loop has no branch and all
-// kFetchDepth loads stay in flight.
+// past the unit reads zero and its store is dropped, so every thread runs the same number
+// of batches and the pipeline has no per-lane branch.
 template <int BM>
 __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid, int row0, int nrows) {
@@ -860,13 +883,14 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
   if (rows.base && span <= 0x7fffffffll) {
     const rsrc_t src = make_rsrc(rows.base, span);
     const rsrc_t dst = make_rsrc(p.staging + m_beg * p.K, span);
-    while (r < R) {
-      u32x4 v[kFetchDepth];
-      uint32_t off[kFetchDepth];
+    const int batches = (R * CR + kThreads * kCopyBatch - 1) / (kThreads * kCopyBatch);
+    u32x4 va[kCopyBatch], vb[kCopyBatch];
+    uint32_t oa[kCopyBatch], ob[kCopyBatch];
+    auto load = [&](u32x4 (&v)[kCopyBatch], uint32_t (&o)[kCopyBatch]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kFetchDepth; ++i) {
-        off[i] = r < R ? (uint32_t)(((int64_t)r * p.K + k_beg + cc * 8) * 2) : kOob;
-        v[i] = bload16(src, off[i]);
+      for (int i = 0; i < kCopyBatch; ++i) {
+        o[i] = r < R ? (uint32_t)(((int64_t)r * p.K + k_beg + cc * 8) * 2) : kOob;
+        v[i] = bload16(src, o[i]);
         r += dr;
         cc += dc;
         if (cc >= CR) {
@@ -874,8 +898,17 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
           ++r;
         }
       }
+    };
+    auto store = [&](const u32x4 (&v)[kCopyBatch], const uint32_t (&o)[kCopyBatch]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kFetchDepth; ++i) bstore16(dst, off[i], v[i]);
+      for (int i = 0; i < kCopyBatch; ++i) bstore16(dst, o[i], v[i]);
+    };
+    load(va, oa);
+    for (int n = 0; n < batches; n += 2) {
+      load(vb, ob);  // past the last batch: all out of range
+      store(va, oa);
+      if (n + 2 < batches) load(va, oa);
+      store(vb, ob);
     }
     return;
   }
@@ -893,14 +926,14 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
 }
 
 // Copy unit (t_m, g) into m_contiguous staging: each thread transposes 8x8 blocks (8 rows x
-// 8 K values), four at a time. Block (kb, mb) is numbered b with kb = (b / (8 NBM)) * 8 +
+// 8 K values), NB per batch. Block (kb, mb) is numbered b with kb = (b / (8 NBM)) * 8 +
 // b % 8 and mb = (b / 8) % NBM, so 8 consecutive lanes read 128 contiguous bytes of one row;
 // a thread's blocks b, b + 256, ... advance (kb, mb) by fixed steps (no division). Same
-// buffer-access fast path as the k_contiguous copy.
+// buffer-access fast path and pipeline as the k_contiguous copy.
 template <int BM>
 __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid, int row0, int nrows) {
-  constexpr int NB = kFetchDepth / 8;  // blocks per thread in flight
+  constexpr int NB = kCopyBatch / 8;  // blocks per thread and batch
   const int64_t m_beg = (int64_t)t_m * BM + row0;
   const int R = (int)min((int64_t)nrows, p.M - m_beg);    // multiple of 8
   const int64_t k_beg = (int64_t)g * KG;
@@ -916,15 +949,17 @@ __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards
   if (rows.base && sspan <= 0x7fffffffll && dspan <= 0x7fffffffll) {
     const rsrc_t src = make_rsrc(rows.base, sspan);
     const rsrc_t dst = make_rsrc(p.staging + k_beg * p.M + m_beg, dspan - m_beg * 2);
-    while (kbh * 8 < NBK) {
-      u32x4 v[NB][8];
-      uint32_t doff[NB];
+    const int tt = ((NBK + 7) / 8) * NBM;  // values of t
+    const int batches = (tt + (kThreads / 8) * NB - 1) / ((kThreads / 8) * NB);
+    u32x4 va[NB][8], vb[NB][8];
+    uint32_t da[NB], db[NB];
+    auto load = [&](u32x4 (&v)[NB][8], uint32_t (&d)[NB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
         const int kb = kbh * 8 + lo;
-        const bool ok = kb < NBK;
+        const bool ok = kb < NBK;  // also false for every t past the unit
         const uint32_t soff = (uint32_t)((((int64_t)mb * 8) * p.K + k_beg + kb * 8) * 2);
-        doff[q] = ok ? (uint32_t)(((int64_t)kb * 8 * p.M + mb * 8) * 2) : kOob;
+        d[q] = ok ? (uint32_t)(((int64_t)kb * 8 * p.M + mb * 8) * 2) : kOob;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           v[q][j] = bload16(src, ok ? soff + (uint32_t)(j * p.K * 2) : kOob);
@@ -935,12 +970,21 @@ __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards
           ++kbh;
         }
       }
+    };
+    auto store = [&](const u32x4 (&v)[NB][8], const uint32_t (&d)[NB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < NB; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          bstore16(dst, doff[q] == kOob ? kOob : doff[q] + (uint32_t)(i * p.M * 2),
+          bstore16(dst, d[q] == kOob ? kOob : d[q] + (uint32_t)(i * p.M * 2),
                    transpose_row(v[q], i));
+    };
+    load(va, da);
+    for (int n = 0; n < batches; n += 2) {
+      load(vb, db);  // past the last batch: all out of range
+      store(va, da);
+      if (n + 2 < batches) load(va, da);
+      store(vb, db);
     }
     return;
   }
@@ -1035,17 +1079,11 @@ __device__ inline int grab(const KParams& p) {
 template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
-  // the four stages, contiguous: a stage's base is then arithmetic on the first one's
-  // address, also where the stage index is only known at run time (the epilogue)
-  __shared__ u32x4 lds_stages[4 * T::STAGE];
+  // the stages, contiguous: a stage's base is then arithmetic on the first one's address,
+  // also where the stage index is only known at run time (the epilogue)
+  __shared__ u32x4 lds_stages[T::NS * T::STAGE];
   __shared__ u32x2 s_bias[T::BN / 4];
-  Stages<T> st;
-  const uint32_t lds_base = (uint32_t)(size_t)(lds_void*)lds_stages;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.s[i] = (lds_u32x4*)lds_stages + i * T::STAGE;
-    st.off[i] = lds_base + (uint32_t)(i * T::STAGE * 16);
-  }
+  const Stages<T> st{(lds_u32x4*)lds_stages, (uint32_t)(size_t)(lds_void*)lds_stages};
   __shared__ int s_next, s_last, s_claim;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
