@@ -12,7 +12,8 @@ Parity pins (each checked by ``tests/test_oracle_*.py`` against something other 
 oracle itself): 16-bit decode exhaustively against numpy / bit reinterpretation; RNE encode
 against round-trips, all midpoints and numpy's double->half rounding; the contraction
 against exact rational brute force, a library fp64 matmul, identity / permutation / zero B,
-shard-count invariance, exact-integer inputs and the hand-written shard-order fixture.
+shard-count invariance, exact-integer inputs and the hand-written shard-order fixture; the
+gathered A against its closed form (each shard filled with its own index and row number).
 """
 from __future__ import annotations
 
@@ -63,6 +64,8 @@ def _load():
     lib.oracle_check.argtypes = [ctypes.c_int, ctypes.c_int64, u16p, f64p, ctypes.c_double,
                                  ctypes.c_double, f64p, f64p, i64p]
     lib.oracle_check.restype = ctypes.c_int64
+    lib.oracle_all_gather.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.POINTER(u16p), u16p]
     _lib = lib
     return lib
 
@@ -142,6 +145,20 @@ def agmm(dtype, shards: Sequence[np.ndarray], B: np.ndarray, bias: Optional[np.n
                                 C.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
                                 out16.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
     return C, out16, int(used)
+
+
+def all_gather(shards: Sequence[np.ndarray]) -> np.ndarray:
+    """The gathered A, [D * M_s, K] uint16: shard d's rows at rows d*M_s .. (d+1)*M_s - 1."""
+    lib = _load()
+    D = len(shards)
+    M_s, K = shards[0].shape
+    for s in shards:
+        if s.shape != (M_s, K):
+            raise ValueError("all shards must have the same shape")
+    args = _Args(shards, np.zeros((0, 0), dtype=np.uint16), None)
+    A = np.empty((D * M_s, K), dtype=np.uint16)
+    lib.oracle_all_gather(D, M_s, K, args.ptrs, A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
+    return A
 
 
 def agmm_at(dtype, shards: Sequence[np.ndarray], B: np.ndarray, bias: Optional[np.ndarray],

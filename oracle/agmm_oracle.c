@@ -176,6 +176,18 @@ int oracle_agmm_rows(int dtype, int D, int64_t M, int64_t N, int64_t K,
   return used;
 }
 
+/*
+ * The gathered A itself, the first result of the op a = all_gather(a_shared) (same
+ * comment as above): A_out[i][k] = A[i][k] for i in [0, D*M_s), a bit copy, row by row.
+ */
+void oracle_all_gather(int D, int64_t M_s, int64_t K, const uint16_t* const* shards,
+                       uint16_t* A_out) {
+  for (int64_t i = 0; i < (int64_t)D * M_s; ++i) {
+    const uint16_t* src = gathered_row(shards, M_s, K, i);
+    for (int64_t k = 0; k < K; ++k) A_out[i * K + k] = src[k];
+  }
+}
+
 /* Selected outputs one by one: C_out[s] = C[rows[s]][cols[s]] (unrounded). */
 void oracle_agmm_at(int dtype, int D, int64_t M, int64_t N, int64_t K,
                     const uint16_t* const* shards, const uint16_t* B, const uint16_t* bias,

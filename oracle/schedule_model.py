@@ -20,7 +20,9 @@ bit for bit:
   staged S'  = [t in S if not direct(t)]
   units      = staged m-tiles grouped by the round in which the queues first reach them
                (entries in (i, x) order, the k-th in round k // W); window by window, GEMM
-               order inside a window: for g in 0..G-1: for t in window: (t, g)
+               order inside a window: for g in 0..G-1: for t in window: (t, g); with
+               gather_a (the op also returns a = all_gather(a_shared), Kraken comment), then
+               the direct m-tiles: for g in 0..G-1: for t in direct, GEMM order: (t, g)
   claims     = fetchers take units in increasing u from one counter (so the units of one
                workgroup ascend); every unit is claimed exactly once
   queues     = GEMM-order m-tiles in super-rows of 4; a super-row's tiles listed in column
@@ -56,6 +58,7 @@ class Geometry:
     num_cus: int = 256      # compute units of the device
     num_wgs_req: int = 0    # requested grid size (0 = one workgroup per compute unit)
     tail_split: int = 0     # 1 = split the tail tiles along K (0: never)
+    gather_a: bool = False  # the run also returns the gathered A: direct m-tiles fetched too
 
     @property
     def M_s(self) -> int:
@@ -181,6 +184,11 @@ def fetch_units(g: Geometry) -> List[Tuple[int, int]]:
             for _, pos in staged[i:j]:
                 units.append((order[pos], kg))
         i = j
+    if g.gather_a:
+        direct = [t for t in order if is_direct(g, t)]
+        for kg in range(g.G):
+            for t in direct:
+                units.append((t, kg))
     return units
 
 

@@ -4,6 +4,8 @@ exactly once, every output tile computed exactly once, local-shard m-tiles never
 the local shard's m-tiles first in GEMM order, shards visited in rank-rotated order."""
 import itertools
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -24,6 +26,20 @@ def test_hand_example_two_shards():
     assert sm.gemm_tiles(g) == [(0, 0), (0, 1), (1, 0), (1, 1)]
     assert sm.fetch_units(g) == [(1, 0), (1, 1)]
     assert list(sm.expected_flags(g, 7)) == [0, 0, 7, 7]
+
+
+def test_hand_example_gather_a():
+    # the op also returns the gathered A: after the staged unit(s), the direct m-tiles'
+    # units, k-group by k-group in GEMM order; every m-tile's flags then hold the epoch
+    g = geo(gather_a=True)
+    assert sm.fetch_units(g) == [(1, 0), (1, 1), (0, 0), (0, 1)]
+    assert list(sm.expected_flags(g, 5)) == [5, 5, 5, 5]
+    # rank 2 of 4, M_s = 2, BM = 2: own m-tile 2 last
+    g2 = geo(D=4, M=8, BM=2, rank=2, N=2, BN=2, W=2, F=1, K=2, k_per_flag=2, gather_a=True)
+    assert sm.fetch_units(g2) == [(3, 0), (0, 0), (1, 0), (2, 0)]
+    # nothing read in place: gather_a adds no unit
+    g3 = geo(direct_local=False)
+    assert sm.fetch_units(g3) == sm.fetch_units(dataclasses.replace(g3, gather_a=True))
 
 
 def test_hand_example_256_row_tile_flags():
