@@ -7,8 +7,8 @@ error codes into exceptions. Every step of the computation runs in the library's
 there is no fallback path. If libagmm.so is missing, importing this module raises.
 
 The functions mirror the C names: ag_matmul_desc_init, ag_matmul_create, ag_matmul_run,
-ag_matmul_destroy, ag_matmul_workspace_bytes, ag_matmul_strerror, ag_matmul_get_config,
-ag_matmul_debug_query, ag_matmul_debug_fill_staging. `AgMatmul` wraps a handle for torch
+ag_matmul_run_gather, ag_matmul_destroy, ag_matmul_workspace_bytes, ag_matmul_strerror,
+ag_matmul_get_config, ag_matmul_debug_query, ag_matmul_debug_fill_staging. `AgMatmul` wraps a handle for torch
 tensors (data pointers and torch's current stream only).
 """
 from __future__ import annotations
@@ -37,6 +37,7 @@ EXPORTED = [
     "ag_matmul_desc_init", "ag_matmul_create", "ag_matmul_run", "ag_matmul_destroy",
     "ag_matmul_workspace_bytes", "ag_matmul_strerror", "ag_matmul_last_hip_error",
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
+    "ag_matmul_run_gather",
 ]
 
 
@@ -50,7 +51,7 @@ class agmm_desc(ctypes.Structure):
         ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
         ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("gather_a", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -98,6 +99,7 @@ def _load():
     lib.ag_matmul_desc_init.restype = None
     lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp)]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.ag_matmul_run_gather.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]
     lib.ag_matmul_destroy.argtypes = [vp]
     lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
@@ -139,6 +141,15 @@ def ag_matmul_run(handle: int, shard_ptrs: Sequence[int], B_ptr: int, bias_ptr: 
     return lib.ag_matmul_run(ctypes.c_void_p(handle), arr, ctypes.c_void_p(B_ptr),
                              ctypes.c_void_p(bias_ptr) if bias_ptr else None,
                              ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
+
+
+def ag_matmul_run_gather(handle: int, shard_ptrs: Sequence[int], B_ptr: int,
+                         bias_ptr: Optional[int], out_ptr: int, a_ptr: int, stream: int = 0) -> int:
+    arr = (ctypes.c_void_p * max(1, len(shard_ptrs)))(*[ctypes.c_void_p(p) for p in shard_ptrs])
+    return lib.ag_matmul_run_gather(ctypes.c_void_p(handle), arr, ctypes.c_void_p(B_ptr),
+                                    ctypes.c_void_p(bias_ptr) if bias_ptr else None,
+                                    ctypes.c_void_p(out_ptr), ctypes.c_void_p(a_ptr),
+                                    ctypes.c_void_p(stream))
 
 
 def ag_matmul_destroy(handle: Optional[int]) -> int:
@@ -185,17 +196,20 @@ def ag_matmul_debug_fill_staging(handle: int, pattern: int, stream: int = 0) -> 
 
 class AgMatmul:
     """One handle for one problem shape. run() takes D shard tensors [M/D, K], B [K, N],
-    an optional bias [N] and an output [M, N], all contiguous on the handle's device."""
+    an optional bias [N] and an output [M, N], all contiguous on the handle's device.
+    With gather_a=True, run() also takes (or allocates) a_out [M, K], which receives the
+    gathered A, and returns (a_out, out)."""
 
     def __init__(self, D: int, M: int, N: int, K: int, dtype="f16", layout="k_contiguous",
                  algo="fused", rank: int = 0, direct_local: bool = True, has_bias: bool = False,
-                 debug: bool = False, **tunables):
+                 debug: bool = False, gather_a: bool = False, **tunables):
         self.desc = ag_matmul_desc_init(
             D=D, M=M, N=N, K=K, rank=rank,
             dtype={"f16": F16, "bf16": BF16}[dtype],
             layout={"k_contiguous": K_CONTIGUOUS, "m_contiguous": M_CONTIGUOUS}[layout],
             algo={"fused": ALGO_FUSED, "baseline": ALGO_BASELINE}[algo],
-            direct_local=int(direct_local), has_bias=int(has_bias), debug=int(debug), **tunables)
+            direct_local=int(direct_local), has_bias=int(has_bias), debug=int(debug),
+            gather_a=int(gather_a), **tunables)
         self.dtype = dtype
         self.handle = ag_matmul_create(self.desc)
         self.config = ag_matmul_get_config(self.handle)
@@ -217,9 +231,11 @@ class AgMatmul:
     def __exit__(self, *exc):
         self.close()
 
-    def run(self, shards, B, bias=None, out=None, stream=None, check: bool = True):
+    def run(self, shards, B, bias=None, out=None, stream=None, check: bool = True, a_out=None):
         import torch
         d = self.desc
+        if a_out is not None and not d.gather_a:
+            raise ValueError("a_out needs a handle created with gather_a=True")
         if len(shards) != d.D:
             raise ValueError(f"expected {d.D} shards, got {len(shards)}")
         tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
@@ -229,6 +245,18 @@ class AgMatmul:
         if out is None:
             out = torch.empty((d.M, d.N), dtype=tdt, device=B.device)
         s = stream if stream is not None else torch.cuda.current_stream(B.device)
+        if d.gather_a:
+            if a_out is None:
+                a_out = torch.empty((d.M, d.K), dtype=tdt, device=B.device)
+            if a_out.dtype != tdt or not a_out.is_cuda or not a_out.is_contiguous() or \
+                    tuple(a_out.shape) != (d.M, d.K):
+                raise ValueError("a_out must be a contiguous [M, K] device tensor of the handle's dtype")
+            rc = ag_matmul_run_gather(self.handle, [t.data_ptr() for t in shards], B.data_ptr(),
+                                      bias.data_ptr() if bias is not None else None,
+                                      out.data_ptr(), a_out.data_ptr(), s.cuda_stream)
+            if check and rc != AGMM_OK:
+                raise AgmmError(rc, "ag_matmul_run_gather")
+            return a_out, out
         rc = ag_matmul_run(self.handle, [t.data_ptr() for t in shards], B.data_ptr(),
                            bias.data_ptr() if bias is not None else None, out.data_ptr(),
                            s.cuda_stream)

@@ -75,6 +75,8 @@ int validate_desc(const agmm_desc* d) {
     return AGMM_ERR_INVALID_ARG;
   if (d->debug_skip_unit < -1) return AGMM_ERR_INVALID_ARG;
   if (d->tail_split != 0 && d->tail_split != 1) return AGMM_ERR_INVALID_ARG;
+  if (d->gather_a != 0 && d->gather_a != 1) return AGMM_ERR_INVALID_ARG;
+  if (d->gather_a && d->layout != AGMM_K_CONTIGUOUS) return AGMM_ERR_UNSUPPORTED;
   if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
   if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
     return AGMM_ERR_UNSUPPORTED;
@@ -184,7 +186,9 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   for (int64_t t : direct) pl->mtiles.push_back((uint32_t)t | 0x80000000u);
   for (int64_t t : other) pl->mtiles.push_back((uint32_t)t);
 
-  const int64_t n_units = (int64_t)other.size() * G;
+  // gather_a: the local shard's m-tiles are fetched too (after every staged one; no tile
+  // waits for them), so that the staging buffer ends up holding all of A.
+  const int64_t n_units = ((int64_t)other.size() + (d.gather_a ? (int64_t)direct.size() : 0)) * G;
   if (n_units >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
   c.num_units = (int32_t)n_units;
 
@@ -270,10 +274,16 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
       }
     ws = we;
   }
+  if (d.gather_a)
+    for (int64_t g = 0; g < G; ++g)
+      for (int64_t t : direct) {
+        pl->units.push_back((uint32_t)t);
+        pl->units.push_back((uint32_t)g);
+      }
 
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
   pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
-  c.staging_elems = n_units > 0 ? d.M * d.K : 0;
+  c.staging_elems = (n_units > 0 && !d.gather_a) ? d.M * d.K : 0;
   pl->flags_n = std::max<int64_t>(1, T_m * G);
 
   int64_t off = 0;
@@ -439,8 +449,14 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg) {
   return AGMM_OK;
 }
 
-int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
-                  void* out, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// gather: called as ag_matmul_run_gather; a_gathered is then the caller's [M, K] buffer,
+// which serves as the staging buffer (NULL allowed only when it has no bytes).
+int run_impl(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
+             void* out, bool gather, void* a_gathered, void* hip_stream) {
   if (!h) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
   const agmm_desc& d = h->desc;
@@ -467,7 +483,18 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
     if (overlaps(out, out_bytes, shards[i], shard_bytes)) return AGMM_ERR_INVALID_ARG;
   if (overlaps(out, out_bytes, B, b_bytes) || overlaps(out, out_bytes, bias, bias_bytes))
     return AGMM_ERR_INVALID_ARG;
-  if (c.num_tiles == 0) return AGMM_OK;  // M == 0 or N == 0: nothing to write
+  if (gather != (d.gather_a != 0)) return AGMM_ERR_INVALID_ARG;
+  if (d.gather_a) {
+    const int64_t a_bytes = d.M * d.K * esz;
+    if ((a_bytes > 0 && !a_gathered) || misaligned(a_gathered)) return AGMM_ERR_INVALID_ARG;
+    if (overlaps(a_gathered, a_bytes, out, out_bytes) || overlaps(a_gathered, a_bytes, B, b_bytes) ||
+        overlaps(a_gathered, a_bytes, bias, bias_bytes))
+      return AGMM_ERR_INVALID_ARG;
+    for (int i = 0; i < d.D; ++i)
+      if (overlaps(a_gathered, a_bytes, shards[i], shard_bytes)) return AGMM_ERR_INVALID_ARG;
+  }
+  // M == 0 or N == 0: no output tile; only a gathered A (N == 0) may have rows to copy
+  if (c.num_tiles == 0 && c.num_units == 0) return AGMM_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
@@ -483,7 +510,7 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
   p.B = static_cast<const uint16_t*>(B);
   p.bias = static_cast<const uint16_t*>(bias);
   p.out = static_cast<uint16_t*>(out);
-  p.staging = h->staging;
+  p.staging = d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging;
   p.flags = h->flags;
   p.ctr = h->ctr;
   p.units = h->units;
@@ -529,7 +556,7 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
     if (c.num_units > 0) AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
     const int grid = (int)std::min<int64_t>(std::min(c.num_cus, c.num_items),
                                             d.num_wgs ? d.num_wgs : c.num_cus);
-    AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
+    if (grid > 0) AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
   }
 
   if (d.debug) {
@@ -542,6 +569,20 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
     }
   }
   return AGMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
+                  void* out, void* hip_stream) {
+  return run_impl(h, shards, B, bias, out, false, nullptr, hip_stream);
+}
+
+int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
+                         const void* bias, void* out, void* a_gathered, void* hip_stream) {
+  return run_impl(h, shards, B, bias, out, true, a_gathered, hip_stream);
 }
 
 int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {

@@ -66,6 +66,38 @@ def bench_workload(w, algo, steps, warmup, torch, A, inputs=None, dev=None, **tu
     return {"wall_s": wall, "per_ms": per, "config": cfg, "inputs": inp, "dev": dev}
 
 
+def gather_variant(w, dev, steps, warmup, torch, A):
+    """The op that also returns the gathered A, (a, out) = ag_matmul(a_shared, b), on the
+    workload's shape with k_contiguous staging (the caller's [M, K] buffer is the staging):
+    median ms of fused and baseline, and of the plain fused run on the same layout, whose
+    difference is the cost of also copying the local shard."""
+    wk = w.with_(layout="k_contiguous")
+    a_out = torch.empty((wk.M, wk.K), dtype=wk.torch_dtype(), device="cuda")
+    res = {"workload": wk.name, "layout": wk.layout}
+    for key, algo, gather in (("fused_ms", "fused", True), ("baseline_ms", "baseline", True),
+                              ("fused_no_gather_ms", "fused", False)):
+        op = A.AgMatmul(wk.D, wk.M, wk.N, wk.K, dtype=wk.dtype, layout=wk.layout, algo=algo,
+                        rank=wk.rank, direct_local=wk.direct_local, has_bias=wk.has_bias,
+                        gather_a=gather)
+        kw = {"a_out": a_out} if gather else {}
+        for _ in range(warmup):
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out, **kw)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False, **kw)
+            b.record()
+        torch.cuda.synchronize()
+        res[key] = round(statistics.median(a.elapsed_time(b) for a, b in ev), 5)
+        op.close()
+    res["fused_speedup"] = round(res["baseline_ms"] / res["fused_ms"], 3)
+    del a_out
+    torch.cuda.empty_cache()
+    return res
+
+
 def yardstick_matmul(w, dev, steps, warmup, torch):
     """torch.matmul on a pre-gathered A (library GEMM, context only)."""
     Ag = torch.cat(dev.shards, 0)
@@ -267,6 +299,7 @@ def main():
         ym = yardstick_matmul(w, r["dev"], args.steps, args.warmup, torch)
         res["yardstick_torch_matmul_pregathered"] = {
             "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}
+        res["gather_a_variant"] = gather_variant(w, r["dev"], args.steps, args.warmup, torch, A)
         # staging traffic of the fused step: 2 * (staged rows) * K * 2 bytes (read + write)
         staged_bytes = 2 * (w.M - (w.M_s if w.direct_local else 0)) * w.K * 2
         res["staging"] = {"bytes_per_step": staged_bytes,

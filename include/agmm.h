@@ -91,21 +91,28 @@ typedef struct agmm_desc {
                             workgroup has work; 0 (default): never split. Measured on the
                             16384x3584x8192 workload the dynamic tile queues already even
                             out most of that round and the split does not pay. */
-  int32_t reserved[2];
+  int32_t gather_a;      /* 1: a run also returns the gathered A, concat(shards) as [M, K]
+                            row-major, in a caller buffer that serves as the staging buffer
+                            (ag_matmul_run_gather; ag_matmul_run is then refused). The
+                            fetch also copies the local shard's tiles, which the GEMM still
+                            reads in place. k_contiguous only (UNSUPPORTED otherwise). */
+  int32_t reserved[1];
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
 typedef struct agmm_config {
   int32_t block_m, block_n, block_k, k_per_flag;
   int32_t T_m, T_n, G;          /* m-tiles, n-tiles, k-groups (one flag per m-tile x k-group) */
-  int32_t num_units;            /* staged (m-tile, k-group) units */
+  int32_t num_units;            /* (m-tile, k-group) units the fetch copies: the staged ones,
+                                   then, with gather_a and direct_local, the local shard's */
   int32_t num_tiles;            /* output tiles */
   int32_t num_fetch_wgs;        /* F */
   int32_t num_wgs;              /* W, fused grid (fetchers included) */
   int32_t num_copy_wgs;         /* baseline copy-kernel grid */
   int32_t trace_cap;
   uint32_t epoch;               /* epoch of the last run (0 before the first) */
-  int64_t staging_elems;        /* 16-bit elements in the staging buffer */
+  int64_t staging_elems;        /* 16-bit elements in the handle's staging buffer (0 with
+                                   gather_a: the caller's buffer is the staging) */
   int64_t workspace_bytes;      /* device bytes the handle owns */
   int32_t device;               /* HIP device the handle was created on */
   int32_t num_cus;
@@ -127,7 +134,7 @@ void ag_matmul_desc_init(agmm_desc* desc);
 /*
  * Creates a handle for one problem shape on the current HIP device: validates `desc`,
  * chooses the tile configuration, and allocates and zeroes the workspace (staging buffer
- * of M*K elements, flags[T_m*G] uint32, schedule tables, counters, optional trace). This is
+ * of M*K elements unless gather_a, flags[T_m*G] uint32, schedule tables, counters, optional trace). This is
  * the preamble of the iris issue ("API / config changes": ..._preamble), done once so that
  * run() allocates nothing.
  * Returns AGMM_OK and *out_handle, or INVALID_ARG / UNSUPPORTED / OOM / HIP.
@@ -146,10 +153,24 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
  * Every device pointer must be 16-byte aligned. The caller keeps all buffers alive until
  * the stream work completes. One run may be in flight per handle; successive runs on one
  * stream are safe; concurrent runs of one handle on different streams are undefined.
- * Returns AGMM_OK, INVALID_ARG, WRONG_DEVICE, POISONED, HIP, or (debug) TIMEOUT.
+ * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
+ * or (debug) TIMEOUT.
  */
 int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
                   void* out, void* hip_stream);
+
+/*
+ * The run of a gather_a handle: as ag_matmul_run, and it also writes the all-gathered A
+ * (Helion thread, Kraken optimization comment: the op returns a = all_gather(a_shared) with
+ * out = a @ b):
+ *   a_gathered: device [M, K] row-major, 16-byte aligned, must not overlap any other
+ *               buffer; row m = row m - d*M/D of shard d. It is the run's staging buffer:
+ *               its contents are undefined until the stream work completes.
+ * Returns AGMM_OK, or INVALID_ARG (also for a handle without gather_a), WRONG_DEVICE,
+ * POISONED, HIP, or (debug) TIMEOUT.
+ */
+int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
+                         const void* bias, void* out, void* a_gathered, void* hip_stream);
 
 /* Synchronizes the handle's device and frees its workspace. NULL-safe. */
 int ag_matmul_destroy(agmm_handle* h);

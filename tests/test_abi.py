@@ -73,6 +73,8 @@ def test_validation_errors(A):
     assert _ws(A, D=1, M=1 << 23, N=8, K=8) == UNS
     assert _ws(A, D=1, M=8, N=8, K=8, has_bias=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, tail_split=2) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, gather_a=2) == INV
+    assert _ws(A, D=2, M=16, N=8, K=8, gather_a=1, layout=A.M_CONTIGUOUS) == UNS
     # create rejects before touching a device
     with pytest.raises(A.AgmmError) as e:
         A.ag_matmul_create(A.ag_matmul_desc_init(D=0))
@@ -80,6 +82,7 @@ def test_validation_errors(A):
     # NULL handles
     assert A.ag_matmul_destroy(None) == 0
     assert A.lib.ag_matmul_run(None, None, None, None, None, None) == INV
+    assert A.lib.ag_matmul_run_gather(None, None, None, None, None, None, None) == INV
 
 
 def test_workspace_bytes_large(A):
@@ -102,6 +105,11 @@ def test_workspace_bytes_large(A):
     assert got - got3 == al(128 * 4) - al(4) + al(1024 * 4) - al(896 * 4) + al(256 * 256 * 256 * 4)
     # D=1 with direct reads: nothing staged, no staging buffer
     assert _ws(A, D=1, M=1024, N=1024, K=1024, block_m=128) < 1 << 16
+    # gather_a: the caller's buffer is the staging (none in the workspace), and the local
+    # shard's 8 m-tiles x 16 k-groups join the unit records
+    got4 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, gather_a=1)
+    got5 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256)
+    assert got5 - got4 == al(16384 * 8192 * 2) + al(56 * 16 * 8) - al(64 * 16 * 8)
 
 
 def test_struct_layout_matches_header(A, tmp_path):

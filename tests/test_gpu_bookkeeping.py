@@ -164,3 +164,60 @@ def test_flag_wait_is_bounded():
     assert rc2 == -7  # POISONED
     torch.cuda.synchronize()
     op.close()
+
+
+@pytest.mark.parametrize("w", CASES[:3], ids=lambda w: w.name)
+@pytest.mark.parametrize("kpf,nf", [(2, 5), (32, 64)], ids=["kloop_waits", "row_waits"])
+def test_gather_a_bookkeeping(w, kpf, nf):
+    """The op that also returns the gathered A: the caller's [M, K] buffer (poisoned with NaN
+    before each run) is the staging buffer; the fetch also copies the local shard's m-tiles,
+    after every staged one. Unit table, flags and trace against the model; the gathered A
+    bit for bit against the oracle's all_gather."""
+    import torch
+    import all_gather_gemm_amd as A
+    import oracle
+    if w.layout != "k_contiguous":
+        w = w.with_(layout="k_contiguous")
+    print(f"case gather {w.name} kpf={kpf} fetchers={nf}", flush=True)
+    inp = make_inputs(w)
+    g_in = inp.to("cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
+                    direct_local=w.direct_local, has_bias=w.has_bias, debug=True, block_m=64,
+                    k_per_flag=kpf, num_fetch_wgs=nf, trace_cap=4096, gather_a=True)
+    cfg = op.config.as_dict()
+    assert cfg["staging_elems"] == 0
+    g = sm.Geometry(w.D, w.M, w.N, w.K, cfg["block_m"], cfg["block_n"], cfg["block_k"],
+                    cfg["k_per_flag"], w.rank, w.direct_local, cfg["num_fetch_wgs"],
+                    cfg["num_wgs"], num_cus=cfg["num_cus"], gather_a=True)
+    units = sm.fetch_units(g)
+    assert [tuple(u) for u in op.units()] == units
+    assert sorted(set(t for t, _ in units)) == list(range(g.T_m))   # every m-tile fetched
+    A_ref = oracle.all_gather([bits(s) for s in inp.shards])
+    C, _ = oracle_full(w, inp)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    a_out = torch.empty((w.M, w.K), dtype=tdt, device="cuda")
+    prior = np.zeros(g.T_m * g.G, dtype=np.uint32)
+    for epoch in (1, 2):
+        a_out.view(torch.int16).fill_(int(np.array(NAN16[w.dtype], np.uint16).view(np.int16)))
+        a, out = op.run(g_in.shards, g_in.B, g_in.bias, a_out=a_out)
+        torch.cuda.synchronize()
+        assert a.data_ptr() == a_out.data_ptr()
+        assert np.array_equal(out_bits(a).reshape(w.M, w.K), A_ref)
+        r = oracle.check(w.dtype, out_bits(out), C)
+        assert r["bad"] == 0, r
+        flags = op.flags()
+        assert np.array_equal(flags, sm.expected_flags(g, epoch, prior))
+        prior = flags.copy()
+        counts, recs = op.trace()
+        fetched = []
+        for wg in range(cfg["num_wgs"]):
+            for rec in recs[wg, :counts[wg]]:
+                if rec["event"] == A.EV_FETCH:
+                    assert wg < g.F
+                    fetched.append(int(rec["id"]))
+                    assert (int(rec["a"]), int(rec["b"])) == units[int(rec["id"])]
+                elif rec["event"] == A.EV_GEMM_WAIT:
+                    assert not sm.is_direct(g, int(rec["id"]) // g.G)   # nobody waits on own tiles
+        assert sorted(fetched) == list(range(len(units)))
+        assert np.array_equal(op.status(), np.zeros(4, dtype=np.uint32))
+    op.close()

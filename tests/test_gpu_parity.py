@@ -205,3 +205,87 @@ def test_tail_split_full_oracle(D, Ms, N, K, dt, layout, bias, nw):
     _, out16 = oracle_full(wi, inpi)
     assert np.array_equal(out_bits(run_gpu(wi, inpi, "fused", **kw).out), out16)
     assert np.array_equal(out_bits(run_gpu(wi, inpi, "baseline", **kw).out), out16)
+
+
+GATHER = [
+    # (D, M_s, N, K, dtype, bias, block_m (0 = auto), rank, direct_local)
+    (2, 136, 264, 1032, "f16", True, 128, 1, True),
+    (4, 72, 520, 200, "bf16", False, 64, 0, True),
+    (3, 200, 328, 424, "f16", True, 256, 2, False),
+    (8, 128, 1024, 1024, "bf16", False, 0, 3, True),
+    (1, 296, 136, 72, "bf16", True, 256, 0, True),
+]
+
+
+@pytest.mark.parametrize("D,Ms,N,K,dt,bias,bm,rank,dl", GATHER)
+def test_gather_a_parity(D, Ms, N, K, dt, bias, bm, rank, dl):
+    """The op that also returns the gathered A ((a, out) = ag_matmul(a_shared, b)): a equals
+    the oracle's all_gather bit for bit, and out equals the plain run's output bit for bit
+    (same kernels, same K order) and the oracle within tolerance; fused and baseline."""
+    import torch
+    import all_gather_gemm_amd as A
+    import oracle
+    from workloads import bits
+    w = Workload(f"gather_{D}x{Ms}_{N}_{K}_{dt}", D, D * Ms, N, K, dt, "normal_sqrtk", bias,
+                 "k_contiguous", dl, 200 + D + K, rank=rank)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    g = inp.to("cuda")
+    A_ref = oracle.all_gather([bits(s) for s in inp.shards])
+    C, _ = oracle_full(w, inp)
+    tun = {"block_m": bm} if bm else {}
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    for algo in ("fused", "baseline"):
+        plain = out_bits(run_gpu(w, inp, algo, dev_inp=g, **tun).out)
+        op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=dt, layout="k_contiguous", algo=algo,
+                        rank=rank, direct_local=dl, has_bias=bias, gather_a=True, **tun)
+        for it in range(2):
+            a_out = torch.full((w.M, w.K), float("nan"), dtype=tdt, device="cuda")
+            a, out = op.run(g.shards, g.B, g.bias, a_out=a_out)
+            torch.cuda.synchronize()
+            assert np.array_equal(out_bits(a).reshape(w.M, w.K), A_ref), (algo, it)
+            assert np.array_equal(out_bits(out), plain), (algo, it)
+        assert_close(w, out_bits(out), C, algo)
+        op.close()
+
+
+def test_gather_a_edge_cases():
+    """N = 0 (no output tile, the gathered A is still written), K = 0 (nothing to gather),
+    and the entry points refusing the wrong kind of handle."""
+    import torch
+    import all_gather_gemm_amd as A
+    import oracle
+    from workloads import bits
+    rng = np.random.default_rng(3)
+    sh = [torch.from_numpy(rng.standard_normal((64, 72)).astype(np.float16)).cuda() for _ in range(2)]
+    A_ref = oracle.all_gather([bits(s.cpu()) for s in sh])
+    for algo in ("fused", "baseline"):
+        op = A.AgMatmul(2, 128, 0, 72, algo=algo, rank=1, gather_a=True)
+        a, out = op.run(sh, torch.zeros((72, 0), dtype=torch.float16, device="cuda"))
+        torch.cuda.synchronize()
+        assert out.shape == (128, 0)
+        assert np.array_equal(out_bits(a).reshape(128, 72), A_ref), algo
+        op.close()
+    op = A.AgMatmul(2, 128, 64, 0, gather_a=True)
+    a, out = op.run([torch.zeros((64, 0), dtype=torch.float16, device="cuda")] * 2,
+                    torch.zeros((0, 64), dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+    assert a.shape == (128, 0) and not out.float().abs().sum().item()
+    op.close()
+    # a gather handle refuses ag_matmul_run; a plain handle refuses ag_matmul_run_gather
+    B = torch.zeros((72, 64), dtype=torch.float16, device="cuda")
+    out = torch.empty((128, 64), dtype=torch.float16, device="cuda")
+    a_out = torch.empty((128, 72), dtype=torch.float16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    ptrs = [t.data_ptr() for t in sh]
+    og = A.AgMatmul(2, 128, 64, 72, gather_a=True)
+    assert A.ag_matmul_run(og.handle, ptrs, B.data_ptr(), None, out.data_ptr(), s) == -1
+    # the gathered A may not alias the output or a shard
+    assert A.ag_matmul_run_gather(og.handle, ptrs, B.data_ptr(), None, out.data_ptr(),
+                                  sh[0].data_ptr(), s) == -1
+    op = A.AgMatmul(2, 128, 64, 72)
+    assert A.ag_matmul_run_gather(op.handle, ptrs, B.data_ptr(), None, out.data_ptr(),
+                                  a_out.data_ptr(), s) == -1
+    torch.cuda.synchronize()
+    og.close()
+    op.close()
