@@ -192,6 +192,26 @@ def fetch_units(g: Geometry) -> List[Tuple[int, int]]:
     return units
 
 
+def pipeline_plan(g: Geometry, chunks_requested: int = 0):
+    """The host stream pipeline (NVIDIA/Fuser PR #3695's AG+GEMM host program): A's rows cut
+    into S chunks along each shard, chunk i = local rows [i*M_s/S, (i+1)*M_s/S) of every
+    shard. S is the request (default 4) lowered until M_s is a multiple of S*BM, so that
+    every m-tile lies in one chunk (1 when M_s is not a multiple of BM). Returns (S,
+    [(units of chunk i in fetch order, m-tiles of chunk i in GEMM order)])."""
+    S = chunks_requested or 4
+    if g.M_s == 0 or g.M_s % g.BM:
+        S = 1
+    while S > 1 and g.M_s % (S * g.BM):
+        S -= 1
+    rows = g.M_s // S if S > 1 else 1
+
+    def chunk(t):
+        return 0 if S == 1 else ((t * g.BM) % g.M_s) // rows
+    units, order = fetch_units(g), mtile_order(g)
+    return S, [([u for u in units if chunk(u[0]) == i], [t for t in order if chunk(t) == i])
+               for i in range(S)]
+
+
 def expected_flags(g: Geometry, epoch: int, prior: np.ndarray = None) -> np.ndarray:
     """Flag array [T_m * G] after a run with the given epoch."""
     size = g.T_m * g.G

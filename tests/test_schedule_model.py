@@ -42,6 +42,27 @@ def test_hand_example_gather_a():
     assert sm.fetch_units(g3) == sm.fetch_units(dataclasses.replace(g3, gather_a=True))
 
 
+def test_hand_example_pipeline_chunks():
+    # D=2, M_s=8, BM=2, rank 0 in place: 4 chunks of 2 local rows, so chunk i holds m-tile i
+    # of shard 0 (in place) and m-tile 4+i of shard 1 (staged, all its k-groups)
+    g = geo(M=16, K=4, k_per_flag=2)
+    S, ch = sm.pipeline_plan(g, 4)
+    assert S == 4
+    assert [c[1] for c in ch] == [[0, 4], [1, 5], [2, 6], [3, 7]]
+    assert [c[0] for c in ch] == [[(4 + i, 0), (4 + i, 1)] for i in range(4)]
+    # 2 chunks: local rows 0..3 and 4..7
+    S2, ch2 = sm.pipeline_plan(g, 2)
+    assert S2 == 2 and [c[1] for c in ch2] == [[0, 1, 4, 5], [2, 3, 6, 7]]
+    # lowered: M_s = 6 is not a multiple of 4 * 2, but of 3 * 2; M_s = 5: one chunk
+    assert sm.pipeline_plan(geo(M=12), 4)[0] == 3
+    assert sm.pipeline_plan(geo(M=10), 4)[0] == 1
+    # every unit and m-tile in exactly one chunk
+    for g2 in (g, geo(M=12, rank=1), geo(M=24, D=4, rank=2, direct_local=False)):
+        S3, c3 = sm.pipeline_plan(g2, 0)
+        assert sorted(u for c in c3 for u in c[0]) == sorted(sm.fetch_units(g2))
+        assert sorted(t for c in c3 for t in c[1]) == list(range(g2.T_m))
+
+
 def test_hand_example_256_row_tile_flags():
     # D=2, M=512, BM=256: m-tile 0 is read in place, m-tile 1 is one unit; after run 3 its
     # flag holds 3 and a prior value elsewhere is kept
