@@ -28,9 +28,9 @@ ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "OOM", -5: "TIMEO
           -6: "WRONG_DEVICE", -7: "POISONED"}
 F16, BF16 = 0, 1
 K_CONTIGUOUS, M_CONTIGUOUS = 0, 1
-ALGO_FUSED, ALGO_BASELINE = 0, 1
-Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES, Q_QUEUES, Q_PARTIALS = \
-    range(1, 10)
+ALGO_FUSED, ALGO_BASELINE, ALGO_PIPELINED = 0, 1, 2
+(Q_FLAGS, Q_STAGING, Q_TRACE, Q_TRACE_COUNT, Q_STATUS, Q_UNITS, Q_MTILES, Q_QUEUES, Q_PARTIALS,
+ Q_CHUNK_SIZES, Q_CHUNK_UNITS, Q_CHUNK_MTILES) = range(1, 13)
 EV_FETCH, EV_GEMM, EV_GEMM_WAIT = 1, 2, 3
 
 EXPORTED = [
@@ -51,7 +51,7 @@ class agmm_desc(ctypes.Structure):
         ("num_fetch_wgs", ctypes.c_int32), ("num_wgs", ctypes.c_int32),
         ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
         ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
-        ("gather_a", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
+        ("gather_a", ctypes.c_int32), ("pipeline_chunks", ctypes.c_int32),
     ]
 
 
@@ -66,7 +66,8 @@ class agmm_config(ctypes.Structure):
         ("workspace_bytes", ctypes.c_int64), ("device", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
         ("split_pieces", ctypes.c_int32), ("num_items", ctypes.c_int32),
-        ("row_wait", ctypes.c_int32),
+        ("row_wait", ctypes.c_int32), ("pipeline_chunks", ctypes.c_int32),
+        ("pipeline_streams", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -207,7 +208,7 @@ class AgMatmul:
             D=D, M=M, N=N, K=K, rank=rank,
             dtype={"f16": F16, "bf16": BF16}[dtype],
             layout={"k_contiguous": K_CONTIGUOUS, "m_contiguous": M_CONTIGUOUS}[layout],
-            algo={"fused": ALGO_FUSED, "baseline": ALGO_BASELINE}[algo],
+            algo={"fused": ALGO_FUSED, "baseline": ALGO_BASELINE, "pipelined": ALGO_PIPELINED}[algo],
             direct_local=int(direct_local), has_bias=int(has_bias), debug=int(debug),
             gather_a=int(gather_a), **tunables)
         self.dtype = dtype
@@ -278,6 +279,24 @@ class AgMatmul:
         n = self.config.num_units
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_UNITS, n * 8),
                              dtype="<u4").reshape(-1, 2)
+
+    def chunks(self):
+        """AGMM_ALGO_PIPELINED: per chunk, (units [(m-tile, k-group)], m-tiles in GEMM order
+        with bit 31 = read in place)."""
+        S = self.config.pipeline_chunks
+        sizes = np.frombuffer(ag_matmul_debug_query(self.handle, Q_CHUNK_SIZES, S * 8),
+                              dtype="<u4").reshape(-1, 2)
+        nu, nm = int(sizes[:, 0].sum()), int(sizes[:, 1].sum())
+        units = np.frombuffer(ag_matmul_debug_query(self.handle, Q_CHUNK_UNITS, nu * 8),
+                              dtype="<u4").reshape(-1, 2)
+        mt = np.frombuffer(ag_matmul_debug_query(self.handle, Q_CHUNK_MTILES, nm * 4), dtype="<u4")
+        out, u0, m0 = [], 0, 0
+        for a, b in sizes:
+            out.append(([tuple(int(x) for x in r) for r in units[u0:u0 + a]],
+                        [int(x) for x in mt[m0:m0 + b]]))
+            u0 += int(a)
+            m0 += int(b)
+        return out
 
     def mtiles(self) -> np.ndarray:
         n = self.config.T_m

@@ -11,6 +11,16 @@
 
 using agmm::KParams;
 
+// One chunk of the host stream pipeline: its slices of the chunk tables (units in 2-word
+// records, m-tiles, queue entries) and its queue offsets / lengths inside its entries.
+struct PipeChunk {
+  int32_t u_off, u_len, m_off, m_len, q_off, q_len;
+  int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
+};
+// The nvFuser host program's stream rotation: chunk i runs on stream i % streams, stream 0
+// being the caller's own; the other streams are the handle's.
+constexpr int kPipeStreams = 4;
+
 struct agmm_handle {
   agmm_desc desc;
   agmm_config cfg;
@@ -32,6 +42,12 @@ struct agmm_handle {
   std::vector<uint32_t> h_units, h_mtiles, h_qtiles;
   int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
   bool poisoned;
+  // AGMM_ALGO_PIPELINED
+  std::vector<PipeChunk> chunks;
+  uint32_t *c_units, *c_mtiles, *c_qtiles, *c_ctr;
+  hipStream_t pstreams[kPipeStreams - 1];  // streams 1 .. of the rotation
+  hipEvent_t ev_start, ev_done[kPipeStreams - 1];
+  int n_pstreams, n_events;  // created so far (destroy releases these)
 };
 
 namespace {
@@ -45,6 +61,8 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // ~ several seconds of backed
 constexpr int kDefaultTraceCap = 512;
 constexpr int kTraceWgsAuto = 2048;
 constexpr int kDefaultFetchWgs = 32;  // the iris issue's tuned num_fetch_sms default
+constexpr int kDefaultChunks = 4;     // AGMM_ALGO_PIPELINED: chunks per shard
+constexpr int kMaxChunks = 64;
 
 #define AGMM_HIP(x)                      \
   do {                                   \
@@ -67,7 +85,9 @@ int validate_desc(const agmm_desc* d) {
   if (d->M % d->D != 0) return AGMM_ERR_INVALID_ARG;
   if (d->dtype != AGMM_F16 && d->dtype != AGMM_BF16) return AGMM_ERR_INVALID_ARG;
   if (d->layout != AGMM_K_CONTIGUOUS && d->layout != AGMM_M_CONTIGUOUS) return AGMM_ERR_INVALID_ARG;
-  if (d->algo != AGMM_ALGO_FUSED && d->algo != AGMM_ALGO_BASELINE) return AGMM_ERR_INVALID_ARG;
+  if (d->algo != AGMM_ALGO_FUSED && d->algo != AGMM_ALGO_BASELINE && d->algo != AGMM_ALGO_PIPELINED)
+    return AGMM_ERR_INVALID_ARG;
+  if (d->pipeline_chunks < 0 || d->pipeline_chunks > kMaxChunks) return AGMM_ERR_INVALID_ARG;
   if ((d->direct_local | d->has_bias | d->debug) & ~1) return AGMM_ERR_INVALID_ARG;
   if (d->block_m != 0 && d->block_m != 64 && d->block_m != 128 && d->block_m != 256)
     return AGMM_ERR_INVALID_ARG;
@@ -98,6 +118,10 @@ struct Plan {
   int64_t flags_n, trace_wgs, split_base;
   int64_t off_staging, off_flags, off_ctr, off_split, off_units, off_mtiles, off_qtiles,
       off_partials, off_trace, off_tcount, total;
+  // AGMM_ALGO_PIPELINED: chunk tables, and one counter block per chunk
+  std::vector<PipeChunk> chunks;
+  std::vector<uint32_t> c_units, c_mtiles, c_qtiles;
+  int64_t off_c_ctr, off_c_units, off_c_mtiles, off_c_qtiles;
 };
 
 // Tile queues (one per XCD): GEMM-order m-tiles are taken in super-rows of kSuperRows; a
@@ -112,8 +136,9 @@ constexpr int kColBlock = 8;
 void make_queues(int64_t T_m, int64_t T_n, const std::vector<uint32_t>& mtiles, int S,
                  Plan* pl) {
   std::vector<std::vector<uint32_t>> qs(agmm::kQueueSlots);
-  std::vector<int64_t> pos_of(T_m);
-  for (int64_t pos = 0; pos < T_m; ++pos) pos_of[mtiles[pos] & 0x7fffffffu] = pos;
+  std::vector<int64_t> pos_of(S >= 2 ? T_m : 0);  // split tiles only: m-tile -> position
+  if (S >= 2)
+    for (int64_t pos = 0; pos < T_m; ++pos) pos_of[mtiles[pos] & 0x7fffffffu] = pos;
   auto split = [&](int64_t pos, int64_t n) {
     return S >= 2 && (int64_t)(mtiles[pos] & 0x7fffffffu) * T_n + n >= pl->split_base;
   };
@@ -281,6 +306,48 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
         pl->units.push_back((uint32_t)g);
       }
 
+  // Host stream pipeline: S chunks, chunk i = rows [i*M_s/S, (i+1)*M_s/S) of every shard,
+  // each chunk's tables the global ones filtered to its m-tiles (fetch and GEMM order kept).
+  pl->chunks.clear();
+  pl->c_units.clear();
+  pl->c_mtiles.clear();
+  pl->c_qtiles.clear();
+  if (d.algo == AGMM_ALGO_PIPELINED) {
+    int S = d.pipeline_chunks ? d.pipeline_chunks : kDefaultChunks;
+    if (M_s == 0 || M_s % bm != 0) S = 1;
+    while (S > 1 && M_s % ((int64_t)S * bm) != 0) --S;
+    const int64_t rows = S > 1 ? M_s / S : 1;
+    auto chunk_of = [&](uint32_t t) { return S == 1 ? 0 : (int)((((int64_t)t * bm) % M_s) / rows); };
+    for (int i = 0; i < S; ++i) {
+      PipeChunk ch;
+      memset(&ch, 0, sizeof(ch));
+      ch.u_off = (int32_t)(pl->c_units.size() / 2);
+      for (size_t k = 0; k < pl->units.size(); k += 2)
+        if (chunk_of(pl->units[k]) == i) {
+          pl->c_units.push_back(pl->units[k]);
+          pl->c_units.push_back(pl->units[k + 1]);
+        }
+      ch.u_len = (int32_t)(pl->c_units.size() / 2) - ch.u_off;
+      std::vector<uint32_t> mt;
+      for (uint32_t e : pl->mtiles)
+        if (chunk_of(e & 0x7fffffffu) == i) mt.push_back(e);
+      ch.m_off = (int32_t)pl->c_mtiles.size();
+      ch.m_len = (int32_t)mt.size();
+      pl->c_mtiles.insert(pl->c_mtiles.end(), mt.begin(), mt.end());
+      Plan q;
+      q.split_base = 0;
+      make_queues((int64_t)mt.size(), T_n, mt, 0, &q);
+      ch.q_off = (int32_t)pl->c_qtiles.size();
+      ch.q_len = (int32_t)q.qtiles.size();
+      memcpy(ch.qoff, q.qoff, sizeof(ch.qoff));
+      memcpy(ch.qlen, q.qlen, sizeof(ch.qlen));
+      pl->c_qtiles.insert(pl->c_qtiles.end(), q.qtiles.begin(), q.qtiles.end());
+      pl->chunks.push_back(ch);
+    }
+    c.pipeline_chunks = S;
+    c.pipeline_streams = std::min(S, kPipeStreams);
+  }
+
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
   pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
   c.staging_elems = (n_units > 0 && !d.gather_a) ? d.M * d.K : 0;
@@ -297,6 +364,10 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   pl->off_partials = off; off = align256(off + tail * S * (int64_t)bm * bm * 4);
   pl->off_trace = off;   off = align256(off + pl->trace_wgs * c.trace_cap * (int64_t)sizeof(agmm_trace_rec));
   pl->off_tcount = off;  off = align256(off + std::max<int64_t>(1, pl->trace_wgs) * 4);
+  pl->off_c_ctr = off;   off = align256(off + (int64_t)pl->chunks.size() * agmm::CTR_WORDS * 4);
+  pl->off_c_units = off; off = align256(off + (int64_t)pl->c_units.size() * 4);
+  pl->off_c_mtiles = off; off = align256(off + (int64_t)pl->c_mtiles.size() * 4);
+  pl->off_c_qtiles = off; off = align256(off + (int64_t)pl->c_qtiles.size() * 4);
   pl->total = off;
   c.workspace_bytes = off;
   return AGMM_OK;
@@ -309,6 +380,15 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 }
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+// Destroys the pipeline's streams and events created so far (errors ignored: teardown).
+void release_streams(agmm_handle* h) {
+  for (int j = 0; j < h->n_pstreams; ++j) (void)hipStreamDestroy(h->pstreams[j]);
+  if (h->n_events > 0) (void)hipEventDestroy(h->ev_start);
+  for (int j = 0; j + 1 < h->n_events; ++j) (void)hipEventDestroy(h->ev_done[j]);
+  h->n_pstreams = 0;
+  h->n_events = 0;
+}
 
 }  // namespace
 
@@ -381,6 +461,9 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   memcpy(h->qoff, pl.qoff, sizeof(h->qoff));
   memcpy(h->qlen, pl.qlen, sizeof(h->qlen));
   h->poisoned = false;
+  h->chunks = pl.chunks;
+  h->n_pstreams = 0;
+  h->n_events = 0;
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)pl.total);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
@@ -399,9 +482,14 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   h->split_base = pl.split_base;
   h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
   h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
+  h->c_ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_ctr);
+  h->c_units = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_units);
+  h->c_mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_mtiles);
+  h->c_qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_qtiles);
 
   auto fail = [&](hipError_t err) {
     g_last_hip = (int)err;
+    release_streams(h);
     (void)hipFree(h->ws);
     delete h;
     return AGMM_ERR_HIP;
@@ -422,6 +510,32 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   if (!pl.qtiles.empty() &&
       (e = hipMemcpy(h->qtiles, pl.qtiles.data(), pl.qtiles.size() * 4, hipMemcpyHostToDevice)) != hipSuccess)
     return fail(e);
+  if (!pl.chunks.empty()) {
+    if ((e = hipMemset(h->c_ctr, 0, pl.chunks.size() * agmm::CTR_WORDS * 4)) != hipSuccess)
+      return fail(e);
+    const std::vector<uint32_t>* tabs[3] = {&pl.c_units, &pl.c_mtiles, &pl.c_qtiles};
+    uint32_t* dsts[3] = {h->c_units, h->c_mtiles, h->c_qtiles};
+    for (int k = 0; k < 3; ++k)
+      if (!tabs[k]->empty() &&
+          (e = hipMemcpy(dsts[k], tabs[k]->data(), tabs[k]->size() * 4, hipMemcpyHostToDevice)) !=
+              hipSuccess)
+        return fail(e);
+    // default-priority streams that do not synchronize with the null stream (stream 0 of
+    // the rotation is the caller's)
+    for (int j = 1; j < pl.cfg.pipeline_streams; ++j) {
+      if ((e = hipStreamCreateWithFlags(&h->pstreams[j - 1], hipStreamNonBlocking)) != hipSuccess)
+        return fail(e);
+      ++h->n_pstreams;
+    }
+    if ((e = hipEventCreateWithFlags(&h->ev_start, hipEventDisableTiming)) != hipSuccess)
+      return fail(e);
+    ++h->n_events;
+    for (int j = 1; j < pl.cfg.pipeline_streams; ++j) {
+      if ((e = hipEventCreateWithFlags(&h->ev_done[j - 1], hipEventDisableTiming)) != hipSuccess)
+        return fail(e);
+      ++h->n_events;
+    }
+  }
   if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
   *out_handle = h;
   return AGMM_OK;
@@ -433,6 +547,7 @@ int ag_matmul_destroy(agmm_handle* h) {
   int cur = 0;
   if (hipGetDevice(&cur) == hipSuccess && cur != h->cfg.device) (void)hipSetDevice(h->cfg.device);
   hipError_t e = hipDeviceSynchronize();
+  release_streams(h);
   if (e == hipSuccess) e = hipFree(h->ws);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
@@ -548,6 +663,40 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
     p.staged_kmajor = d.layout == AGMM_K_CONTIGUOUS ? 1 : 0;
     p.row_wait = c.row_wait;
     AGMM_HIP(agmm::launch_fused(p, d.dtype, c.block_m, c.num_wgs, s));
+  } else if (d.algo == AGMM_ALGO_PIPELINED) {
+    p.F = 0;
+    p.staged_kmajor = 1;  // chunks gather into plain [M][K] rows
+    p.debug = 0;
+    p.trace_cap = 0;
+    const int ns = c.pipeline_streams;
+    if (ns > 1) {
+      AGMM_HIP(hipEventRecord(h->ev_start, s));
+      for (int j = 1; j < ns; ++j) AGMM_HIP(hipStreamWaitEvent(h->pstreams[j - 1], h->ev_start, 0));
+    }
+    for (size_t i = 0; i < h->chunks.size(); ++i) {
+      const PipeChunk& ch = h->chunks[i];
+      hipStream_t sj = i % ns == 0 ? s : h->pstreams[i % ns - 1];
+      KParams q = p;
+      q.units = h->c_units + 2 * (int64_t)ch.u_off;
+      q.num_units = ch.u_len;
+      q.mtiles = h->c_mtiles + ch.m_off;
+      q.T_m = ch.m_len;
+      q.qtiles = h->c_qtiles + ch.q_off;
+      memcpy(q.qoff, ch.qoff, sizeof(q.qoff));
+      memcpy(q.qlen, ch.qlen, sizeof(q.qlen));
+      q.ctr = h->c_ctr + (int64_t)i * agmm::CTR_WORDS;
+      q.num_tiles = ch.m_len * c.T_n;
+      // the chunk's gather, then (same stream) the chunk's GEMM
+      if (ch.u_len > 0)
+        AGMM_HIP(agmm::launch_copy(q, c.block_m, (int)std::min<int64_t>(ch.u_len, 4LL * c.num_cus), sj));
+      const int grid = (int)std::min<int64_t>(std::min<int64_t>(c.num_cus, ch.q_len),
+                                              d.num_wgs ? d.num_wgs : c.num_cus);
+      if (grid > 0) AGMM_HIP(agmm::launch_gemm_only(q, d.dtype, c.block_m, grid, sj));
+    }
+    for (int j = 1; j < ns; ++j) {
+      AGMM_HIP(hipEventRecord(h->ev_done[j - 1], h->pstreams[j - 1]));
+      AGMM_HIP(hipStreamWaitEvent(s, h->ev_done[j - 1], 0));
+    }
   } else {
     p.F = 0;
     p.staged_kmajor = 1;  // the baseline gathers into plain [M][K] rows
@@ -621,6 +770,23 @@ int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
         memcpy(o + 2 * agmm::kQueueSlots, h->h_qtiles.data(), h->h_qtiles.size() * 4);
       return AGMM_OK;
     }
+    case AGMM_Q_CHUNK_SIZES: {
+      if (bytes != h->chunks.size() * 8) return AGMM_ERR_INVALID_ARG;
+      uint32_t* o = static_cast<uint32_t*>(dst);
+      for (size_t i = 0; i < h->chunks.size(); ++i) {
+        o[2 * i] = (uint32_t)h->chunks[i].u_len;
+        o[2 * i + 1] = (uint32_t)h->chunks[i].m_len;
+      }
+      return AGMM_OK;
+    }
+    case AGMM_Q_CHUNK_UNITS:
+      src = h->c_units;
+      for (const PipeChunk& ch : h->chunks) n += (size_t)ch.u_len * 8;
+      break;
+    case AGMM_Q_CHUNK_MTILES:
+      src = h->c_mtiles;
+      for (const PipeChunk& ch : h->chunks) n += (size_t)ch.m_len * 4;
+      break;
     default: return AGMM_ERR_INVALID_ARG;
   }
   if (bytes != n) return AGMM_ERR_INVALID_ARG;

@@ -25,10 +25,6 @@ constexpr int kQueueSlots = kQueues + 1;
 constexpr uint32_t kItemTileMask = 0x00ffffffu;
 constexpr int kMaxSplit = 4;
 
-// A fetch unit (m-tile x k-group) is copied in pieces of kPieceRows rows, claimed one by
-// one from a global counter; a unit's flag counts its finished pieces (BM / kPieceRows per
-// run, so after run e it holds e * BM / kPieceRows).
-
 // Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
 enum : int {
   CTR_DONE = 0,         // workgroups that finished; the last one resets the queue counters

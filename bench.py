@@ -9,9 +9,11 @@ every launch on the launch stream (the fused path is one kernel per step, so the
 time that kernel). TFLOP/s counts 2*M*N*K per step with M the full gathered row count, the
 convention of the iris issue's results tables.
 
-Prints ONE JSON line on stdout. `--sweep` additionally writes a table of all five workloads
-(fused, copy-barrier-GEMM baseline, and torch.matmul on pre-gathered A as a yardstick) to
-stderr and, with --out, to a JSON-lines file.
+Prints ONE JSON line on stdout. Unless --no-extras, the line also carries the other
+variants on the same inputs: the copy-barrier-GEMM baseline, the host stream pipeline
+(2, 4, 8 chunks), the variant that also returns the gathered A, and torch.matmul on a
+pre-gathered A as a yardstick. `--sweep` additionally writes a table of all five workloads
+(fused, baseline, pipelined, yardstick) to stderr and, with --out, to a JSON-lines file.
 """
 import argparse
 import json
@@ -178,7 +180,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ag_16384x3584x8192_d8_f16_bias")
-    ap.add_argument("--algo", default="fused", choices=["fused", "baseline"])
+    ap.add_argument("--algo", default="fused", choices=["fused", "baseline", "pipelined"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -231,12 +233,17 @@ def main():
             rf = bench_workload(w, "fused", args.steps, args.warmup, torch, A, **tun)
             rb = bench_workload(w, "baseline", args.steps, args.warmup, torch, A,
                                 inputs=rf["inputs"], dev=rf["dev"], **tun)
+            rp = bench_workload(w, "pipelined", args.steps, args.warmup, torch, A,
+                                inputs=rf["inputs"], dev=rf["dev"], **tun)
             ym = yardstick_matmul(w, rf["dev"], args.steps, args.warmup, torch)
             mf, mb = statistics.median(rf["per_ms"]), statistics.median(rb["per_ms"])
+            mp = statistics.median(rp["per_ms"])
             row = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "D": w.D,
                    "dtype": w.dtype, "layout": w.layout,
                    "fused_ms_median": mf, "fused_ms_min": min(rf["per_ms"]),
                    "baseline_ms_median": mb, "speedup": mb / mf,
+                   "pipelined_ms_median": mp,
+                   "pipelined_chunks": rp["config"]["pipeline_chunks"],
                    "fused_tflops": tflops(w.M, w.N, w.K, mf / 1e3),
                    "baseline_tflops": tflops(w.M, w.N, w.K, mb / 1e3),
                    "pct_peak": 100 * tflops(w.M, w.N, w.K, mf / 1e3) / PEAK_TFLOPS[w.dtype],
@@ -244,10 +251,11 @@ def main():
                    "fetch_wgs": rf["config"]["num_fetch_wgs"], "wgs": rf["config"]["num_wgs"]}
             rows.append(row)
             print("| {workload} | {fused_ms_median:.4f} | {baseline_ms_median:.4f} | "
+                  "{pipelined_ms_median:.4f} (S={pipelined_chunks}) | "
                   "{speedup:.2f}x | {fused_tflops:.1f} | {pct_peak:.1f}% | "
                   "{torch_matmul_pregathered_ms:.4f} | {block_m} |".format(**row),
                   file=sys.stderr, flush=True)
-            del rf, rb
+            del rf, rb, rp
             torch.cuda.empty_cache()
         if args.out:
             with open(args.out, "w") as fh:
@@ -300,6 +308,16 @@ def main():
         res["yardstick_torch_matmul_pregathered"] = {
             "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}
         res["gather_a_variant"] = gather_variant(w, r["dev"], args.steps, args.warmup, torch, A)
+        # the host stream pipeline (chunked copy + GEMM-only kernels rotating over 4 streams)
+        pv = {}
+        for S in (2, 4, 8):
+            rp = bench_workload(w, "pipelined", args.steps, args.warmup, torch, A,
+                                inputs=r["inputs"], dev=r["dev"], pipeline_chunks=S, **tun)
+            pv[f"chunks_{rp['config']['pipeline_chunks']}_median_ms"] = round(
+                statistics.median(rp["per_ms"]), 5)
+        pv["fused_speedup_vs_best"] = round(min(pv.values()) / statistics.median(per), 3) \
+            if args.algo == "fused" else None
+        res["pipelined_variant"] = pv
         # staging traffic of the fused step: 2 * (staged rows) * K * 2 bytes (read + write)
         staged_bytes = 2 * (w.M - (w.M_s if w.direct_local else 0)) * w.K * 2
         res["staging"] = {"bytes_per_step": staged_bytes,

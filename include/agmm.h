@@ -62,6 +62,14 @@ extern "C" {
 
 #define AGMM_ALGO_FUSED 0     /* fetcher + GEMM workgroups in one persistent kernel */
 #define AGMM_ALGO_BASELINE 1  /* copy kernel, then stream order (the barrier), then GEMM */
+/* Host stream pipeline (NVIDIA/Fuser PR #3695, the AG+GEMM host program: A's rows cut into S
+ * chunks along each shard, and for chunk i, on stream i % streams (stream 0 being the
+ * caller's), the chunk's all-gather, a wait for it, then the chunk's GEMM; the caller's
+ * stream then waits for every other stream).
+ * Chunk i holds rows [i*M_s/S, (i+1)*M_s/S) of every shard; here the chunk's gather is the
+ * copy kernel over its staged units and its GEMM the GEMM-only kernel over its m-tiles, so
+ * one chunk's copy overlaps another chunk's GEMM without flags. Staging is [M][K]. */
+#define AGMM_ALGO_PIPELINED 2
 
 /* Problem and tuning description. Fields marked "0 = auto" are chosen by create. */
 typedef struct agmm_desc {
@@ -70,7 +78,7 @@ typedef struct agmm_desc {
   int64_t M, N, K;       /* gathered rows (M = D * M_shard), columns, inner dimension */
   int32_t dtype;         /* AGMM_F16 or AGMM_BF16 for shards, B, bias and out */
   int32_t layout;        /* AGMM_K_CONTIGUOUS or AGMM_M_CONTIGUOUS (fused algorithm) */
-  int32_t algo;          /* AGMM_ALGO_FUSED or AGMM_ALGO_BASELINE */
+  int32_t algo;          /* AGMM_ALGO_FUSED, AGMM_ALGO_BASELINE or AGMM_ALGO_PIPELINED */
   int32_t direct_local;  /* 1: local-shard tiles read in place; 0: every tile staged */
   int32_t has_bias;      /* 1: run() takes a bias[N] pointer; 0: bias must be NULL */
   int32_t debug;         /* 1: record per-workgroup trace; run() synchronizes and reports
@@ -96,7 +104,9 @@ typedef struct agmm_desc {
                             (ag_matmul_run_gather; ag_matmul_run is then refused). The
                             fetch also copies the local shard's tiles, which the GEMM still
                             reads in place. k_contiguous only (UNSUPPORTED otherwise). */
-  int32_t reserved[1];
+  int32_t pipeline_chunks; /* AGMM_ALGO_PIPELINED: chunks S per shard; 0 = auto (4). Lowered
+                              to the largest S with M/D a multiple of S * block_m (1 when
+                              M/D is not a multiple of block_m) */
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
@@ -123,6 +133,9 @@ typedef struct agmm_config {
                                    whole fetch is one pass); a tile then waits at its start for
                                    all of its k-groups and its K loop never polls. 0: the K loop
                                    waits for each staged k-group as it reaches it */
+  int32_t pipeline_chunks;      /* AGMM_ALGO_PIPELINED: chunks S actually used (0 otherwise) */
+  int32_t pipeline_streams;     /* AGMM_ALGO_PIPELINED: streams the chunks rotate over, min(S, 4):
+                                   the caller's, and pipeline_streams - 1 of the handle's */
 } agmm_config;
 
 typedef struct agmm_handle agmm_handle;
@@ -206,6 +219,12 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg);
                                  (tile, piece); inside a slot, element i of accumulator group
                                  (fm, fn, g) of thread tid at ((fm*FN + fn)*4 + g)*1024 +
                                  tid*4 + i (FN = block_n / 64, 256 threads) */
+#define AGMM_Q_CHUNK_SIZES 10 /* AGMM_ALGO_PIPELINED: uint32[2 * pipeline_chunks], per chunk
+                                 (staged units, m-tiles) */
+#define AGMM_Q_CHUNK_UNITS 11 /* uint32[2 * num_units]: (m-tile, k-group), chunk by chunk, each
+                                 chunk's units in fetch order */
+#define AGMM_Q_CHUNK_MTILES 12 /* uint32[T_m]: m-tiles chunk by chunk, each chunk's in GEMM
+                                  order, bit 31 = read in place */
 
 /* Trace events (debug). One record per fetched unit, per computed tile and per flag wait
  * of wave 0, after the per-workgroup event ids of the iris issue (wg_fetch, wg_gemm,

@@ -75,6 +75,9 @@ def test_validation_errors(A):
     assert _ws(A, D=1, M=8, N=8, K=8, tail_split=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, gather_a=2) == INV
     assert _ws(A, D=2, M=16, N=8, K=8, gather_a=1, layout=A.M_CONTIGUOUS) == UNS
+    assert _ws(A, D=1, M=8, N=8, K=8, algo=3) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, algo=A.ALGO_PIPELINED, pipeline_chunks=-1) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, algo=A.ALGO_PIPELINED, pipeline_chunks=65) == INV
     # create rejects before touching a device
     with pytest.raises(A.AgmmError) as e:
         A.ag_matmul_create(A.ag_matmul_desc_init(D=0))
@@ -110,6 +113,10 @@ def test_workspace_bytes_large(A):
     got4 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, gather_a=1)
     got5 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256)
     assert got5 - got4 == al(16384 * 8192 * 2) + al(56 * 16 * 8) - al(64 * 16 * 8)
+    # the host stream pipeline (4 chunks): a counter block per chunk, and the chunk tables
+    # (896 staged units of 2 words, 64 m-tiles, 896 queue entries)
+    got6 = _ws(A, D=8, M=16384, N=3584, K=8192, block_m=256, algo=A.ALGO_PIPELINED)
+    assert got6 - got5 == al(4 * (96 + 9 * 32) * 4) + al(896 * 2 * 4) + al(64 * 4) + al(896 * 4)
 
 
 def test_struct_layout_matches_header(A, tmp_path):

@@ -289,3 +289,96 @@ def test_gather_a_edge_cases():
     torch.cuda.synchronize()
     og.close()
     op.close()
+
+
+PIPE = [
+    # (D, M_s, N, K, dtype, bias, block_m, rank, direct_local, chunks requested)
+    (2, 512, 264, 1032, "f16", True, 128, 1, True, 4),
+    (4, 128, 520, 200, "bf16", False, 64, 0, True, 2),
+    (3, 256, 328, 424, "f16", True, 256, 2, False, 0),
+    (8, 128, 1024, 1024, "bf16", False, 64, 3, True, 4),
+    (2, 200, 136, 72, "bf16", True, 64, 0, True, 4),     # M_s not a multiple of 64: one chunk
+    (1, 512, 136, 264, "f16", False, 128, 0, True, 4),   # D=1: nothing staged
+]
+
+
+@pytest.mark.parametrize("D,Ms,N,K,dt,bias,bm,rank,dl,S", PIPE)
+def test_pipelined_parity(D, Ms, N, K, dt, bias, bm, rank, dl, S):
+    """The host stream pipeline: output bit-identical to the baseline (same GEMM kernel and K
+    order, only the launch schedule differs) and within tolerance of the oracle; chunk
+    tables against the model; every chunk's staged rows written (staging poisoned with NaN
+    before each run); and with gather_a the gathered A bit-exact."""
+    import torch
+    import all_gather_gemm_amd as A
+    import oracle
+    from oracle import schedule_model as sm
+    from workloads import bits
+    w = Workload(f"pipe_{D}x{Ms}_{N}_{K}_{dt}_{S}", D, D * Ms, N, K, dt, "normal_sqrtk", bias,
+                 "k_contiguous", dl, 300 + D + K, rank=rank)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    g = inp.to("cuda")
+    C, _ = oracle_full(w, inp)
+    base = out_bits(run_gpu(w, inp, "baseline", dev_inp=g, block_m=bm).out)
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=dt, algo="pipelined", rank=rank, direct_local=dl,
+                    has_bias=bias, block_m=bm, pipeline_chunks=S)
+    cfg = op.config.as_dict()
+    geo = sm.Geometry(w.D, w.M, w.N, w.K, cfg["block_m"], cfg["block_n"], cfg["block_k"],
+                      cfg["k_per_flag"], rank, dl, cfg["num_fetch_wgs"], cfg["num_wgs"],
+                      num_cus=cfg["num_cus"])
+    S_model, chunks = sm.pipeline_plan(geo, S)
+    assert cfg["pipeline_chunks"] == S_model
+    assert cfg["pipeline_streams"] == min(S_model, 4)
+    got = op.chunks()
+    assert [c[0] for c in got] == [c[0] for c in chunks]
+    assert [[x & 0x7FFFFFFF for x in c[1]] for c in got] == [c[1] for c in chunks]
+    assert [[bool(x >> 31) for x in c[1]] for c in got] == \
+        [[sm.is_direct(geo, t) for t in c[1]] for c in chunks]
+    A_bits = np.concatenate([bits(s) for s in inp.shards])
+    for it in range(3):
+        op.fill_staging(NAN16[dt])
+        out = op.run(g.shards, g.B, g.bias)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), base), it
+        if cfg["staging_elems"]:
+            assert np.array_equal(op.staging(),
+                                  sm.expected_staging(geo, A_bits, "k_contiguous", NAN16[dt]))
+    assert_close(w, out_bits(out), C, "pipelined")
+    op.close()
+    # the pipeline with the gathered A returned as well
+    opg = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=dt, algo="pipelined", rank=rank, direct_local=dl,
+                     has_bias=bias, block_m=bm, pipeline_chunks=S, gather_a=True)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    a_out = torch.full((w.M, w.K), float("nan"), dtype=tdt, device="cuda")
+    a, out = opg.run(g.shards, g.B, g.bias, a_out=a_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(a).reshape(w.M, w.K), oracle.all_gather(list(map(bits, inp.shards))))
+    assert np.array_equal(out_bits(out), base)
+    opg.close()
+
+
+def test_pipelined_back_to_back_on_a_side_stream():
+    """Runs enqueued back to back on a non-default caller stream with alternating inputs:
+    every run's chunk streams start after the caller's earlier work and the caller's stream
+    waits for all of them, so each output matches its own input's baseline."""
+    import torch
+    import all_gather_gemm_amd as A
+    w = Workload("pipe_alt", 4, 4 * 256, 392, 520, "f16", "normal_sqrtk", True, "k_contiguous",
+                 True, 61, rank=2)
+    sets = [make_inputs(w, seed=s) for s in (61, 62)]
+    dev = [s.to("cuda") for s in sets]
+    refs = [out_bits(run_gpu(w, s, "baseline", dev_inp=d, block_m=64).out)
+            for s, d in zip(sets, dev)]
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, algo="pipelined", rank=w.rank, has_bias=True,
+                    block_m=64, pipeline_chunks=4)
+    side = torch.cuda.Stream()
+    outs = [torch.empty((w.M, w.N), dtype=torch.float16, device="cuda") for _ in range(6)]
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for it in range(6):
+            i = it % 2
+            op.run(dev[i].shards, dev[i].B, dev[i].bias, out=outs[it], stream=side)
+    side.synchronize()
+    for it in range(6):
+        assert np.array_equal(out_bits(outs[it]), refs[it % 2]), it
+    op.close()
