@@ -149,7 +149,8 @@ void ag_matmul_desc_init(agmm_desc* desc);
  * chooses the tile configuration, and allocates and zeroes the workspace (staging buffer
  * of M*K elements unless gather_a, flags[T_m*G] uint32, schedule tables, counters, optional trace). This is
  * the preamble of the iris issue ("API / config changes": ..._preamble), done once so that
- * run() allocates nothing.
+ * run() allocates nothing. AGMM_ALGO_PIPELINED handles also create their HIP streams (up to
+ * 3, default priority, non-blocking) and events here.
  * Returns AGMM_OK and *out_handle, or INVALID_ARG / UNSUPPORTED / OOM / HIP.
  * Shape rules: M % D == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows); m_contiguous also
  * needs M % 8 == 0. M, N, K may be zero (run() then only writes what exists: K == 0 gives
@@ -185,7 +186,8 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream);
 
-/* Synchronizes the handle's device and frees its workspace. NULL-safe. */
+/* Synchronizes the handle's device and frees its workspace (and a pipelined handle's
+ * streams and events). NULL-safe. */
 int ag_matmul_destroy(agmm_handle* h);
 
 /* Device bytes create would allocate for `desc` (after resolving auto fields), or a
