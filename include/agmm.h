@@ -83,9 +83,14 @@ typedef struct agmm_desc {
   int32_t has_bias;      /* 1: run() takes a bias[N] pointer; 0: bias must be NULL */
   int32_t debug;         /* 1: record per-workgroup trace; run() synchronizes and reports
                             a flag-wait timeout as AGMM_ERR_TIMEOUT */
-  int32_t block_m;       /* output tile edge: 64, 128 or 256 (tile is square); 0 = auto */
-  int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto (512 columns when
-                            K >= 4096, else 1024) */
+  int32_t block_m;       /* output tile edge: 64, 128 or 256 (tile is square); 0 = auto: the
+                            largest with at least 3/4 of a tile per CU; fused, 128 instead
+                            of 64 when 64-row tiles would leave fewer than 32 CUs for the
+                            fetchers and 128-row tiles still give a quarter of the CUs one */
+  int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto: 512 columns when
+                            K >= 4096 or in the fused 128-row case above, else 1024; fused
+                            with K >= 4096 and every tile in one round beside 32 spare
+                            workgroups, 256 */
   int32_t num_fetch_wgs; /* fetcher workgroups (fused); 0 = auto: 32, or one per fetch unit
                             when all tiles fit in one round with fewer than 32 workgroups
                             to spare */
