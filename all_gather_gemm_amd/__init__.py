@@ -37,7 +37,7 @@ EXPORTED = [
     "ag_matmul_desc_init", "ag_matmul_create", "ag_matmul_run", "ag_matmul_destroy",
     "ag_matmul_workspace_bytes", "ag_matmul_strerror", "ag_matmul_last_hip_error",
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
-    "ag_matmul_run_gather",
+    "ag_matmul_run_gather", "ag_matmul_plan_query",
 ]
 
 
@@ -101,6 +101,8 @@ def _load():
     lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp)]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.ag_matmul_run_gather.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]
+    lib.ag_matmul_plan_query.argtypes = [ctypes.POINTER(agmm_desc), ctypes.c_int, ctypes.c_int,
+                                         vp, ctypes.c_size_t]
     lib.ag_matmul_destroy.argtypes = [vp]
     lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
@@ -151,6 +153,35 @@ def ag_matmul_run_gather(handle: int, shard_ptrs: Sequence[int], B_ptr: int,
                                     ctypes.c_void_p(bias_ptr) if bias_ptr else None,
                                     ctypes.c_void_p(out_ptr), ctypes.c_void_p(a_ptr),
                                     ctypes.c_void_p(stream))
+
+
+def ag_matmul_plan_query(desc: agmm_desc, num_cus: int = 256) -> dict:
+    """The planner's decisions for `desc` on a device with `num_cus` CUs (host only): the
+    config and every schedule table, as ag_matmul_debug_query lays them out."""
+    def q(what, nbytes, buf=None):
+        buf = buf if buf is not None else (ctypes.c_uint8 * max(1, nbytes))()
+        rc = lib.ag_matmul_plan_query(ctypes.byref(desc), num_cus, what, ctypes.byref(buf), nbytes)
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_matmul_plan_query")
+        return buf
+    cfg = q(0, ctypes.sizeof(agmm_config), agmm_config())
+    u32 = lambda what, n: np.frombuffer(bytes(q(what, n * 4))[:n * 4], dtype="<u4")
+    out = {"config": cfg,
+           "units": u32(Q_UNITS, 2 * cfg.num_units).reshape(-1, 2),
+           "mtiles": u32(Q_MTILES, cfg.T_m)}
+    raw = u32(Q_QUEUES, 2 * 9 + cfg.num_items)
+    out["queues"] = [list(map(int, raw[18 + raw[x]:18 + raw[x] + raw[9 + x]])) for x in range(9)]
+    if cfg.pipeline_chunks:
+        sizes = u32(Q_CHUNK_SIZES, 2 * cfg.pipeline_chunks).reshape(-1, 2)
+        cu = u32(Q_CHUNK_UNITS, 2 * int(sizes[:, 0].sum())).reshape(-1, 2)
+        cm = u32(Q_CHUNK_MTILES, int(sizes[:, 1].sum()))
+        chunks, u0, m0 = [], 0, 0
+        for a, b in sizes:
+            chunks.append(([tuple(map(int, r)) for r in cu[u0:u0 + a]], list(map(int, cm[m0:m0 + b]))))
+            u0 += int(a)
+            m0 += int(b)
+        out["chunks"] = chunks
+    return out
 
 
 def ag_matmul_destroy(handle: Optional[int]) -> int:

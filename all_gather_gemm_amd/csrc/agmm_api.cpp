@@ -818,6 +818,45 @@ int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {
   return AGMM_OK;
 }
 
+int ag_matmul_plan_query(const agmm_desc* desc, int num_cus, int what, void* dst, size_t bytes) {
+  if (!dst || num_cus < 1) return AGMM_ERR_INVALID_ARG;
+  int rc = validate_desc(desc);
+  if (rc != AGMM_OK) return rc;
+  Plan pl;
+  rc = make_plan(*desc, num_cus, &pl);
+  if (rc != AGMM_OK) return rc;
+  auto put = [&](const void* src, size_t n) {
+    if (bytes != n) return AGMM_ERR_INVALID_ARG;
+    if (n) memcpy(dst, src, n);
+    return AGMM_OK;
+  };
+  switch (what) {
+    case 0: return put(&pl.cfg, sizeof(agmm_config));
+    case AGMM_Q_UNITS: return put(pl.units.data(), pl.units.size() * 4);
+    case AGMM_Q_MTILES: return put(pl.mtiles.data(), pl.mtiles.size() * 4);
+    case AGMM_Q_QUEUES: {
+      std::vector<uint32_t> v(2 * agmm::kQueueSlots);
+      for (int x = 0; x < agmm::kQueueSlots; ++x) {
+        v[x] = (uint32_t)pl.qoff[x];
+        v[agmm::kQueueSlots + x] = (uint32_t)pl.qlen[x];
+      }
+      v.insert(v.end(), pl.qtiles.begin(), pl.qtiles.end());
+      return put(v.data(), v.size() * 4);
+    }
+    case AGMM_Q_CHUNK_SIZES: {
+      std::vector<uint32_t> v;
+      for (const PipeChunk& ch : pl.chunks) {
+        v.push_back((uint32_t)ch.u_len);
+        v.push_back((uint32_t)ch.m_len);
+      }
+      return put(v.data(), v.size() * 4);
+    }
+    case AGMM_Q_CHUNK_UNITS: return put(pl.c_units.data(), pl.c_units.size() * 4);
+    case AGMM_Q_CHUNK_MTILES: return put(pl.c_mtiles.data(), pl.c_mtiles.size() * 4);
+    default: return AGMM_ERR_INVALID_ARG;
+  }
+}
+
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {
   if (!h) return AGMM_ERR_INVALID_ARG;
   int cur = 0;

@@ -249,6 +249,14 @@ typedef struct agmm_trace_rec {
  * buffer's size). Synchronizes the device first. */
 int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes);
 
+/* Host only, for tests of the planner: what create would decide for `desc` on a device with
+ * `num_cus` compute units, computed without touching any device. what = 0: the resolved
+ * agmm_config (epoch, device and workspace fields as create sets them before allocating);
+ * otherwise one of AGMM_Q_UNITS, AGMM_Q_MTILES, AGMM_Q_QUEUES, AGMM_Q_CHUNK_SIZES,
+ * AGMM_Q_CHUNK_UNITS, AGMM_Q_CHUNK_MTILES, laid out as ag_matmul_debug_query returns them.
+ * `bytes` must equal the size of the result. Returns AGMM_OK, INVALID_ARG or UNSUPPORTED. */
+int ag_matmul_plan_query(const agmm_desc* desc, int num_cus, int what, void* dst, size_t bytes);
+
 /* Fills the staging buffer with a 16-bit pattern (a NaN pattern exposes reads of unwritten
  * staging) on `hip_stream`. */
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream);
