@@ -196,8 +196,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the multi-GPU path is a design, not code, here)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              "multi-GPU pull over xGMI is designed but not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

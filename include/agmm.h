@@ -41,7 +41,7 @@ extern "C" {
 /* ---- return codes ---- */
 #define AGMM_OK 0
 #define AGMM_ERR_INVALID_ARG (-1)  /* null / misaligned pointer, bad count, aliasing output */
-#define AGMM_ERR_UNSUPPORTED (-2)  /* a shape or option this build does not handle */
+#define AGMM_ERR_UNSUPPORTED (-2)  /* a shape or option the library does not handle */
 #define AGMM_ERR_HIP (-3)          /* a HIP runtime call failed; see ag_matmul_last_hip_error */
 #define AGMM_ERR_OOM (-4)          /* device allocation failed */
 #define AGMM_ERR_TIMEOUT (-5)      /* a flag wait exceeded its spin limit; handle is poisoned */
