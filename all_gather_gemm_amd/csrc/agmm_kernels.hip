@@ -698,16 +698,21 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
                     __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 1)),
                     __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 2)),
                     __builtin_bit_cast(uint32_t, acc_read(acc[fm][fn], 4 * g + 3))};
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Published as a fetch unit is: every wave's stores acknowledged, a barrier, one
+    // agent-scope release by thread 0 (one L2 write-back, not one per wave); the piece that
+    // completes the tile acquires once, in wave 0, before the barrier that lets the other
+    // waves read the slots (an acquire invalidates the XCD's L2 under every tile there).
+    wait_vmcnt<0>();
     __syncthreads();
     if (tid == 0) {
-      const uint32_t done = __hip_atomic_fetch_add(p.split_cnt + sidx, 1u, __ATOMIC_ACQ_REL,
+      const uint32_t done = __hip_atomic_fetch_add(p.split_cnt + sidx, 1u, __ATOMIC_RELEASE,
                                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
-      *is_last = done == (uint32_t)pieces * p.epoch;  // counters grow by `pieces` per run
+      const bool last = done == (uint32_t)pieces * p.epoch;  // counters grow by `pieces` per run
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *is_last = last;
     }
     __syncthreads();
     if (!*is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     parts = slots;
     finish_split = true;
   }
