@@ -54,6 +54,43 @@ def time_runs(op, dev, steps, warmup, torch):
     return wall, per
 
 
+def interleaved(w, algos, steps, warmup, torch, A, inputs=None, dev=None, **tun):
+    """Median ms per op of several variants on the same inputs, their runs alternating on one
+    stream (forward, then backward order), so that clock drift, the power limit's state and
+    allocator state fall on every variant alike. A variant is an algorithm name, or a tuple
+    (name, algorithm, extra tunables). Returns ({name: median_ms}, {name: config}, inputs,
+    dev)."""
+    from workloads import make_inputs
+    inp = inputs if inputs is not None else make_inputs(w)
+    if dev is None:
+        dev = inp.to("cuda")
+        dev.out = torch.empty((w.M, w.N), dtype=w.torch_dtype(), device="cuda")
+    ops = []
+    for v in algos:
+        name, algo, kw = (v, v, {}) if isinstance(v, str) else v
+        ops.append((name, A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout,
+                                     algo=algo, rank=w.rank, direct_local=w.direct_local,
+                                     has_bias=w.has_bias, **{**tun, **kw})))
+    for _ in range(warmup):
+        for _, op in ops:
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out)
+    torch.cuda.synchronize()
+    ev = {name: [] for name, _ in ops}
+    for i in range(steps):
+        for a, op in (ops if i % 2 == 0 else ops[::-1]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+            e1.record()
+            ev[a].append((e0, e1))
+    torch.cuda.synchronize()
+    med = {a: statistics.median(e0.elapsed_time(e1) for e0, e1 in v) for a, v in ev.items()}
+    cfgs = {a: op.config.as_dict() for a, op in ops}
+    for _, op in ops:
+        op.close()
+    return med, cfgs, inp, dev
+
+
 def bench_workload(w, algo, steps, warmup, torch, A, inputs=None, dev=None, **tun):
     from workloads import make_inputs
     inp = inputs if inputs is not None else make_inputs(w)
@@ -72,27 +109,32 @@ def gather_variant(w, dev, steps, warmup, torch, A):
     """The op that also returns the gathered A, (a, out) = ag_matmul(a_shared, b), on the
     workload's shape with k_contiguous staging (the caller's [M, K] buffer is the staging):
     median ms of fused and baseline, and of the plain fused run on the same layout, whose
-    difference is the cost of also copying the local shard."""
+    difference is the cost of also copying the local shard. Runs interleaved on one stream."""
     wk = w.with_(layout="k_contiguous")
     a_out = torch.empty((wk.M, wk.K), dtype=wk.torch_dtype(), device="cuda")
-    res = {"workload": wk.name, "layout": wk.layout}
+    ops = []
     for key, algo, gather in (("fused_ms", "fused", True), ("baseline_ms", "baseline", True),
                               ("fused_no_gather_ms", "fused", False)):
-        op = A.AgMatmul(wk.D, wk.M, wk.N, wk.K, dtype=wk.dtype, layout=wk.layout, algo=algo,
-                        rank=wk.rank, direct_local=wk.direct_local, has_bias=wk.has_bias,
-                        gather_a=gather)
-        kw = {"a_out": a_out} if gather else {}
-        for _ in range(warmup):
+        ops.append((key, A.AgMatmul(wk.D, wk.M, wk.N, wk.K, dtype=wk.dtype, layout=wk.layout,
+                                    algo=algo, rank=wk.rank, direct_local=wk.direct_local,
+                                    has_bias=wk.has_bias, gather_a=gather),
+                    {"a_out": a_out} if gather else {}))
+    for _ in range(warmup):
+        for _, op, kw in ops:
             op.run(dev.shards, dev.B, dev.bias, out=dev.out, **kw)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        torch.cuda.synchronize()
-        for a, b in ev:
-            a.record()
+    torch.cuda.synchronize()
+    ev = {key: [] for key, _, _ in ops}
+    for i in range(steps):
+        for key, op, kw in (ops if i % 2 == 0 else ops[::-1]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False, **kw)
-            b.record()
-        torch.cuda.synchronize()
-        res[key] = round(statistics.median(a.elapsed_time(b) for a, b in ev), 5)
+            e1.record()
+            ev[key].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {"workload": wk.name, "layout": wk.layout}
+    for key, op, _ in ops:
+        res[key] = round(statistics.median(e0.elapsed_time(e1) for e0, e1 in ev[key]), 5)
         op.close()
     res["fused_speedup"] = round(res["baseline_ms"] / res["fused_ms"], 3)
     del a_out
@@ -230,32 +272,28 @@ def main():
     if args.sweep:
         rows = []
         for w in WORKLOADS:
-            rf = bench_workload(w, "fused", args.steps, args.warmup, torch, A, **tun)
-            rb = bench_workload(w, "baseline", args.steps, args.warmup, torch, A,
-                                inputs=rf["inputs"], dev=rf["dev"], **tun)
-            rp = bench_workload(w, "pipelined", args.steps, args.warmup, torch, A,
-                                inputs=rf["inputs"], dev=rf["dev"], **tun)
-            ym = yardstick_matmul(w, rf["dev"], args.steps, args.warmup, torch)
-            mf, mb = statistics.median(rf["per_ms"]), statistics.median(rb["per_ms"])
-            mp = statistics.median(rp["per_ms"])
+            med, cfgs, _, dev = interleaved(w, ("fused", "baseline", "pipelined"), args.steps,
+                                            args.warmup, torch, A, **tun)
+            ym = yardstick_matmul(w, dev, args.steps, args.warmup, torch)
+            mf, mb, mp = med["fused"], med["baseline"], med["pipelined"]
             row = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "D": w.D,
                    "dtype": w.dtype, "layout": w.layout,
-                   "fused_ms_median": mf, "fused_ms_min": min(rf["per_ms"]),
+                   "fused_ms_median": mf,
                    "baseline_ms_median": mb, "speedup": mb / mf,
                    "pipelined_ms_median": mp,
-                   "pipelined_chunks": rp["config"]["pipeline_chunks"],
+                   "pipelined_chunks": cfgs["pipelined"]["pipeline_chunks"],
                    "fused_tflops": tflops(w.M, w.N, w.K, mf / 1e3),
                    "baseline_tflops": tflops(w.M, w.N, w.K, mb / 1e3),
                    "pct_peak": 100 * tflops(w.M, w.N, w.K, mf / 1e3) / PEAK_TFLOPS[w.dtype],
-                   "torch_matmul_pregathered_ms": ym, "block_m": rf["config"]["block_m"],
-                   "fetch_wgs": rf["config"]["num_fetch_wgs"], "wgs": rf["config"]["num_wgs"]}
+                   "torch_matmul_pregathered_ms": ym, "block_m": cfgs["fused"]["block_m"],
+                   "fetch_wgs": cfgs["fused"]["num_fetch_wgs"], "wgs": cfgs["fused"]["num_wgs"]}
             rows.append(row)
             print("| {workload} | {fused_ms_median:.4f} | {baseline_ms_median:.4f} | "
                   "{pipelined_ms_median:.4f} (S={pipelined_chunks}) | "
                   "{speedup:.2f}x | {fused_tflops:.1f} | {pct_peak:.1f}% | "
                   "{torch_matmul_pregathered_ms:.4f} | {block_m} |".format(**row),
                   file=sys.stderr, flush=True)
-            del rf, rb, rp
+            del dev
             torch.cuda.empty_cache()
         if args.out:
             with open(args.out, "w") as fh:
@@ -297,28 +335,29 @@ def main():
     if not args.no_cpu_baseline:   # before the extras reuse the output buffer
         res["cpu_baseline"] = cpu_baseline(w, r["inputs"], r["dev"].out, args.cpu_seconds)
     if not args.no_extras:
+        # the other algorithm, timed interleaved with this one (runs alternating on one
+        # stream), so the ratio does not depend on which ran first
         other = "baseline" if args.algo == "fused" else "fused"
-        rb = bench_workload(w, other, args.steps, args.warmup, torch, A, inputs=r["inputs"],
-                            dev=r["dev"], **tun)
-        mb = statistics.median(rb["per_ms"])
+        pipes = [(f"pipelined_{S}", "pipelined", {"pipeline_chunks": S}) for S in (2, 4, 8)]
+        med, cfgs, _, _ = interleaved(w, [args.algo, other] + pipes, args.steps, args.warmup,
+                                      torch, A, inputs=r["inputs"], dev=r["dev"], **tun)
+        mb = med[other]
         res[f"{other}_variant"] = {"median_ms": round(mb, 5),
                                    "tflops": round(tflops(w.M, w.N, w.K, mb / 1e3), 3),
-                                   "fused_speedup": round((mb / statistics.median(per))
+                                   "interleaved_median_ms_this": round(med[args.algo], 5),
+                                   "fused_speedup": round((mb / med[args.algo])
                                                           if other == "baseline" else
-                                                          (statistics.median(per) / mb), 3)}
+                                                          (med[args.algo] / mb), 3)}
         ym = yardstick_matmul(w, r["dev"], args.steps, args.warmup, torch)
         res["yardstick_torch_matmul_pregathered"] = {
             "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}
         res["gather_a_variant"] = gather_variant(w, r["dev"], args.steps, args.warmup, torch, A)
-        # the host stream pipeline (chunked copy + GEMM-only kernels rotating over 4 streams)
-        pv = {}
-        for S in (2, 4, 8):
-            rp = bench_workload(w, "pipelined", args.steps, args.warmup, torch, A,
-                                inputs=r["inputs"], dev=r["dev"], pipeline_chunks=S, **tun)
-            pv[f"chunks_{rp['config']['pipeline_chunks']}_median_ms"] = round(
-                statistics.median(rp["per_ms"]), 5)
-        pv["fused_speedup_vs_best"] = round(min(pv.values()) / statistics.median(per), 3) \
-            if args.algo == "fused" else None
+        # the host stream pipeline (chunked copy + GEMM-only kernels rotating over 4
+        # streams), from the same interleaved runs
+        pv = {f"chunks_{cfgs[n]['pipeline_chunks']}_median_ms": round(med[n], 5)
+              for n, _, _ in pipes}
+        fused_med = med["fused"]
+        pv["fused_speedup_vs_best"] = round(min(med[n] for n, _, _ in pipes) / fused_med, 3)
         res["pipelined_variant"] = pv
         # staging traffic of the fused step: 2 * (staged rows) * K * 2 bytes (read + write)
         staged_bytes = 2 * (w.M - (w.M_s if w.direct_local else 0)) * w.K * 2
