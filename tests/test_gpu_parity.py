@@ -382,3 +382,20 @@ def test_pipelined_back_to_back_on_a_side_stream():
     for it in range(6):
         assert np.array_equal(out_bits(outs[it]), refs[it % 2]), it
     op.close()
+
+
+@pytest.mark.parametrize("Ms,layout", [(8, "k_contiguous"), (8, "m_contiguous"), (1, "m_contiguous"),
+                                       (3, "k_contiguous")])
+def test_sixty_four_shards(Ms, layout):
+    """The most shards the ABI takes (64): every m-tile spans many shards, so the fetch takes
+    its per-row shard lookup path. Fused, baseline and pipelined against the full oracle and
+    against each other bit for bit."""
+    D = 64
+    w = Workload(f"d64_{Ms}_{layout}", D, D * Ms, 136, 264, "f16", "normal_sqrtk", True, layout,
+                 True, 400 + Ms, rank=37)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    C, _ = oracle_full(w, inp)
+    outs = [out_bits(run_gpu(w, inp, algo).out) for algo in ("fused", "baseline", "pipelined")]
+    assert_close(w, outs[0], C, "fused")
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
