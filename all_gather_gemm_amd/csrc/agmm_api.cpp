@@ -213,6 +213,8 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   const int64_t KG = (int64_t)c.k_per_flag * c.block_k;
   const int64_t G = d.K > 0 ? cdiv(d.K, KG) : 0;
   if (T_m * T_n >= kMaxCount || T_m * G >= kMaxCount) return AGMM_ERR_UNSUPPORTED;
+  // queue entries carry the tile id in 24 bits
+  if (T_m * T_n > (int64_t)agmm::kItemTileMask + 1) return AGMM_ERR_UNSUPPORTED;
   c.T_m = (int32_t)T_m;
   c.T_n = (int32_t)T_n;
   c.G = (int32_t)G;
