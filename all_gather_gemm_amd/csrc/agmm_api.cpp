@@ -54,8 +54,12 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-// Per-thread byte offsets inside a tile are 32-bit: 256 rows of a 2^23-element stride fit.
+// Byte offsets inside a tile are 32-bit and a buffer resource spans at most 2^31 - 1 bytes:
+// 256 rows of an N- or K-element stride (output rows, K-major operand rows) must stay below
+// 2^31 bytes, so N and K stay below 2^22; M only strides the m_contiguous staging, 32 rows
+// of it per K-tile, so M may reach 2^23.
 constexpr int64_t kMaxDim = (int64_t)1 << 23;
+constexpr int64_t kMaxDimNK = (int64_t)1 << 22;
 constexpr int64_t kMaxCount = (int64_t)1 << 31;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // ~ several seconds of backed-off polls
 constexpr int kDefaultTraceCap = 512;
@@ -81,7 +85,7 @@ int validate_desc(const agmm_desc* d) {
   if (d->D < 1 || d->D > AGMM_MAX_SHARDS) return AGMM_ERR_INVALID_ARG;
   if (d->rank < 0 || d->rank >= d->D) return AGMM_ERR_INVALID_ARG;
   if (d->M < 0 || d->N < 0 || d->K < 0) return AGMM_ERR_INVALID_ARG;
-  if (d->M >= kMaxDim || d->N >= kMaxDim || d->K >= kMaxDim) return AGMM_ERR_UNSUPPORTED;
+  if (d->M >= kMaxDim || d->N >= kMaxDimNK || d->K >= kMaxDimNK) return AGMM_ERR_UNSUPPORTED;
   if (d->M % d->D != 0) return AGMM_ERR_INVALID_ARG;
   if (d->dtype != AGMM_F16 && d->dtype != AGMM_BF16) return AGMM_ERR_INVALID_ARG;
   if (d->layout != AGMM_K_CONTIGUOUS && d->layout != AGMM_M_CONTIGUOUS) return AGMM_ERR_INVALID_ARG;

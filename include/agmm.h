@@ -159,7 +159,8 @@ void ag_matmul_desc_init(agmm_desc* desc);
  * Returns AGMM_OK and *out_handle, or INVALID_ARG / UNSUPPORTED / OOM / HIP.
  * Shape rules: M % D == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows); m_contiguous also
  * needs M % 8 == 0. M, N, K may be zero (run() then only writes what exists: K == 0 gives
- * out = bias or 0). M, N, K < 2^23, and at most 2^24 output tiles (UNSUPPORTED otherwise).
+ * out = bias or 0). M < 2^23, N and K < 2^22, and at most 2^24 output tiles (UNSUPPORTED
+ * otherwise).
  */
 int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
 

@@ -71,6 +71,9 @@ def test_validation_errors(A):
     assert _ws(A, D=1, M=8, N=8, K=8, block_m=96) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, dtype=2) == INV
     assert _ws(A, D=1, M=1 << 23, N=8, K=8) == UNS
+    assert _ws(A, D=1, M=8, N=1 << 22, K=8) == UNS        # 256 output rows past 2^31 bytes
+    assert _ws(A, D=1, M=8, N=8, K=1 << 22) == UNS        # 256 K-major rows likewise
+    assert _ws(A, D=1, M=8, N=(1 << 22) - 8, K=(1 << 22) - 8) > 0
     assert _ws(A, D=1, M=8, N=8, K=8, has_bias=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, tail_split=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, gather_a=2) == INV
