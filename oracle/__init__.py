@@ -13,7 +13,8 @@ oracle itself): 16-bit decode exhaustively against numpy / bit reinterpretation;
 against round-trips, all midpoints and numpy's double->half rounding; the contraction
 against exact rational brute force, a library fp64 matmul, identity / permutation / zero B,
 shard-count invariance, exact-integer inputs and the hand-written shard-order fixture; the
-gathered A against its closed form (each shard filled with its own index and row number).
+gathered A against its closed form (each shard filled with its own index and row number);
+the all-reduced GEMM against an identity closed form and planted slice mistakes.
 """
 from __future__ import annotations
 
@@ -159,6 +160,17 @@ def all_gather(shards: Sequence[np.ndarray]) -> np.ndarray:
     A = np.empty((D * M_s, K), dtype=np.uint16)
     lib.oracle_all_gather(D, M_s, K, args.ptrs, A.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
     return A
+
+
+def gemm_allreduce(dtype, A_parts: Sequence[np.ndarray], B_parts: Sequence[np.ndarray],
+                   bias: Optional[np.ndarray] = None):
+    """The all-reduced result of the GEMM + all-reduce op (ROCm/iris PR "Let's make Iris'
+    All-reduce the best!", the atomics example): rank r holds A_r [M, K_r] and B_r [K_r, N],
+    and every rank ends with C = sum_r A_r @ B_r (+ bias), which is the product of the
+    column-concatenated A and the row-concatenated B. Returns (C, out16, threads) as agmm."""
+    A = np.concatenate([_u16(a)[0] for a in A_parts], axis=1)
+    B = np.concatenate([_u16(b)[0] for b in B_parts], axis=0)
+    return agmm(dtype, [A], B, bias)
 
 
 def agmm_at(dtype, shards: Sequence[np.ndarray], B: np.ndarray, bias: Optional[np.ndarray],
