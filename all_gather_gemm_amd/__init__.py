@@ -37,7 +37,8 @@ EXPORTED = [
     "ag_matmul_desc_init", "ag_matmul_create", "ag_matmul_run", "ag_matmul_destroy",
     "ag_matmul_workspace_bytes", "ag_matmul_strerror", "ag_matmul_last_hip_error",
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
-    "ag_matmul_run_gather", "ag_matmul_plan_query",
+    "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
+    "ag_gemm_ar_finalize",
 ]
 
 
@@ -103,6 +104,10 @@ def _load():
     lib.ag_matmul_run_gather.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]
     lib.ag_matmul_plan_query.argtypes = [ctypes.POINTER(agmm_desc), ctypes.c_int, ctypes.c_int,
                                          vp, ctypes.c_size_t]
+    lib.ag_gemm_ar_create.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
+    lib.ag_gemm_ar_run.argtypes = [vp, vp, vp, ctypes.POINTER(vp), vp]
+    lib.ag_gemm_ar_finalize.argtypes = [vp, vp, vp, vp, vp]
     lib.ag_matmul_destroy.argtypes = [vp]
     lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
@@ -367,3 +372,58 @@ class AgMatmul:
         rc = ag_matmul_debug_fill_staging(self.handle, pattern, s.cuda_stream)
         if rc != AGMM_OK:
             raise AgmmError(rc, "ag_matmul_debug_fill_staging")
+
+
+class GemmAllReduce:
+    """One rank's share of GEMM + all-reduce (atomics): run() adds A_local @ B_local (fp32)
+    into each of the D result buffers; finalize() rounds one buffer (+ bias) to 16 bits."""
+
+    def __init__(self, D: int, rank: int, M: int, N: int, K_local: int, dtype="f16",
+                 block_m: int = 0):
+        h = ctypes.c_void_p()
+        rc = lib.ag_gemm_ar_create(D, rank, M, N, K_local, {"f16": F16, "bf16": BF16}[dtype],
+                                   block_m, ctypes.byref(h))
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_gemm_ar_create")
+        self.handle, self.D, self.M, self.N, self.K, self.dtype = h.value, D, M, N, K_local, dtype
+        self.config = ag_matmul_get_config(self.handle)
+
+    def close(self):
+        if self.handle:
+            ag_matmul_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, A_local, B_local, C, stream=None, check: bool = True) -> int:
+        import torch
+        if len(C) != self.D:
+            raise ValueError(f"expected {self.D} result buffers")
+        for t in C:
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("result buffers must be contiguous fp32 device tensors")
+        s = stream if stream is not None else torch.cuda.current_stream(A_local.device)
+        arr = (ctypes.c_void_p * self.D)(*[ctypes.c_void_p(t.data_ptr()) for t in C])
+        rc = lib.ag_gemm_ar_run(ctypes.c_void_p(self.handle), ctypes.c_void_p(A_local.data_ptr()),
+                                ctypes.c_void_p(B_local.data_ptr()), arr,
+                                ctypes.c_void_p(s.cuda_stream))
+        if check and rc != AGMM_OK:
+            raise AgmmError(rc, "ag_gemm_ar_run")
+        return rc
+
+    def finalize(self, C, bias=None, out=None, stream=None):
+        import torch
+        tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        if out is None:
+            out = torch.empty((self.M, self.N), dtype=tdt, device=C.device)
+        s = stream if stream is not None else torch.cuda.current_stream(C.device)
+        rc = lib.ag_gemm_ar_finalize(ctypes.c_void_p(self.handle), ctypes.c_void_p(C.data_ptr()),
+                                     ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
+                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_gemm_ar_finalize")
+        return out

@@ -48,6 +48,8 @@ struct agmm_handle {
   hipStream_t pstreams[kPipeStreams - 1];  // streams 1 .. of the rotation
   hipEvent_t ev_start, ev_done[kPipeStreams - 1];
   int n_pstreams, n_events;  // created so far (destroy releases these)
+  // GEMM + all-reduce handles (ag_gemm_ar_create): ranks and this rank; 0 otherwise
+  int32_t ar_D, ar_rank;
 };
 
 namespace {
@@ -594,11 +596,57 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg) {
 
 namespace {
 
+// The launch parameters of a handle's run: its tables and counters, the given buffers.
+KParams run_params(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
+                   void* out, uint16_t* staging, uint32_t epoch) {
+  const agmm_desc& d = h->desc;
+  const agmm_config& c = h->cfg;
+  KParams p;
+  memset(&p, 0, sizeof(p));
+  for (int i = 0; i < d.D; ++i) p.shards[i] = static_cast<const uint16_t*>(shards[i]);
+  p.B = static_cast<const uint16_t*>(B);
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = static_cast<uint16_t*>(out);
+  p.staging = staging;
+  p.flags = h->flags;
+  p.ctr = h->ctr;
+  p.units = h->units;
+  p.mtiles = h->mtiles;
+  p.qtiles = h->qtiles;
+  for (int x = 0; x < agmm::kQueueSlots; ++x) {
+    p.qoff[x] = h->qoff[x];
+    p.qlen[x] = h->qlen[x];
+  }
+  p.partials = h->partials;
+  p.split_cnt = h->split_cnt;
+  p.split_base = (int32_t)h->split_base;
+  p.trace = h->trace;
+  p.trace_count = h->trace_count;
+  p.M = d.M;
+  p.N = d.N;
+  p.K = d.K;
+  p.M_s = h->M_s;
+  p.D = d.D;
+  p.rank = d.rank;
+  p.T_m = c.T_m;
+  p.T_n = c.T_n;
+  p.G = c.G;
+  p.kpf = c.k_per_flag;
+  p.num_units = c.num_units;
+  p.num_tiles = c.num_tiles;
+  p.epoch = epoch;
+  p.debug = d.debug;
+  p.trace_cap = c.trace_cap;
+  p.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpinLimit;
+  p.skip_unit = d.debug ? d.debug_skip_unit : -1;
+  return p;
+}
+
 // gather: called as ag_matmul_run_gather; a_gathered is then the caller's [M, K] buffer,
 // which serves as the staging buffer (NULL allowed only when it has no bytes).
 int run_impl(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
              void* out, bool gather, void* a_gathered, void* hip_stream) {
-  if (!h) return AGMM_ERR_INVALID_ARG;
+  if (!h || h->ar_D) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
@@ -645,44 +693,8 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   }
   const uint32_t epoch = ++h->cfg.epoch;
 
-  KParams p;
-  memset(&p, 0, sizeof(p));
-  for (int i = 0; i < d.D; ++i) p.shards[i] = static_cast<const uint16_t*>(shards[i]);
-  p.B = static_cast<const uint16_t*>(B);
-  p.bias = static_cast<const uint16_t*>(bias);
-  p.out = static_cast<uint16_t*>(out);
-  p.staging = d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging;
-  p.flags = h->flags;
-  p.ctr = h->ctr;
-  p.units = h->units;
-  p.mtiles = h->mtiles;
-  p.qtiles = h->qtiles;
-  for (int x = 0; x < agmm::kQueueSlots; ++x) {
-    p.qoff[x] = h->qoff[x];
-    p.qlen[x] = h->qlen[x];
-  }
-  p.partials = h->partials;
-  p.split_cnt = h->split_cnt;
-  p.split_base = (int32_t)h->split_base;
-  p.trace = h->trace;
-  p.trace_count = h->trace_count;
-  p.M = d.M;
-  p.N = d.N;
-  p.K = d.K;
-  p.M_s = h->M_s;
-  p.D = d.D;
-  p.rank = d.rank;
-  p.T_m = c.T_m;
-  p.T_n = c.T_n;
-  p.G = c.G;
-  p.kpf = c.k_per_flag;
-  p.num_units = c.num_units;
-  p.num_tiles = c.num_tiles;
-  p.epoch = epoch;
-  p.debug = d.debug;
-  p.trace_cap = c.trace_cap;
-  p.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpinLimit;
-  p.skip_unit = d.debug ? d.debug_skip_unit : -1;
+  KParams p = run_params(h, shards, B, bias, out,
+                          d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging, epoch);
 
   if (d.algo == AGMM_ALGO_FUSED) {
     p.F = c.num_fetch_wgs;
@@ -758,6 +770,87 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream) {
   return run_impl(h, shards, B, bias, out, true, a_gathered, hip_stream);
+}
+
+int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, int dtype,
+                      int block_m, agmm_handle** out_handle) {
+  if (!out_handle) return AGMM_ERR_INVALID_ARG;
+  *out_handle = nullptr;
+  if (D < 1 || D > AGMM_MAX_SHARDS || rank < 0 || rank >= D) return AGMM_ERR_INVALID_ARG;
+  // one rank's share is a plain GEMM over its K columns: the planner's one-shard,
+  // read-in-place case (no fetch units, no staging), run by the atomic-epilogue kernel
+  agmm_desc d;
+  ag_matmul_desc_init(&d);
+  d.M = M;
+  d.N = N;
+  d.K = K_local;
+  d.dtype = dtype;
+  d.algo = AGMM_ALGO_BASELINE;
+  d.block_m = block_m;
+  const int rc = ag_matmul_create(&d, out_handle);
+  if (rc != AGMM_OK) return rc;
+  (*out_handle)->ar_D = D;
+  (*out_handle)->ar_rank = rank;
+  return AGMM_OK;
+}
+
+int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, float* const* C,
+                   void* hip_stream) {
+  if (!h || !h->ar_D || !C) return AGMM_ERR_INVALID_ARG;
+  if (h->poisoned) return AGMM_ERR_POISONED;
+  const agmm_desc& d = h->desc;
+  const agmm_config& c = h->cfg;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != c.device) return AGMM_ERR_WRONG_DEVICE;
+  const int64_t a_bytes = d.M * d.K * 2, b_bytes = d.K * d.N * 2, c_bytes = d.M * d.N * 4;
+  if ((a_bytes > 0 && !A_local) || misaligned(A_local)) return AGMM_ERR_INVALID_ARG;
+  if ((b_bytes > 0 && !B_local) || misaligned(B_local)) return AGMM_ERR_INVALID_ARG;
+  for (int r = 0; r < h->ar_D; ++r) {
+    if ((c_bytes > 0 && !C[r]) || misaligned(C[r])) return AGMM_ERR_INVALID_ARG;
+    if (overlaps(C[r], c_bytes, A_local, a_bytes) || overlaps(C[r], c_bytes, B_local, b_bytes))
+      return AGMM_ERR_INVALID_ARG;
+    for (int q = 0; q < r; ++q)
+      if (overlaps(C[r], c_bytes, C[q], c_bytes)) return AGMM_ERR_INVALID_ARG;
+  }
+  if (c.num_tiles == 0) return AGMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap, as in run_impl
+    AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
+    AGMM_HIP(agmm::launch_fill32(h->split_cnt, c.split_tiles, 0u, s));
+    h->cfg.epoch = 0;
+  }
+  const uint32_t epoch = ++h->cfg.epoch;
+  const void* shards[1] = {A_local};
+  KParams p = run_params(h, shards, B_local, nullptr, nullptr, h->staging, epoch);
+  p.F = 0;
+  p.staged_kmajor = 1;
+  p.debug = 0;
+  p.trace_cap = 0;
+  p.ar_D = h->ar_D;
+  p.ar_rank = h->ar_rank;
+  for (int r = 0; r < h->ar_D; ++r) p.ar_out[r] = C[r];
+  const int grid = (int)std::min<int64_t>(c.num_cus, c.num_items);
+  AGMM_HIP(agmm::launch_gemm_ar(p, d.dtype, c.block_m, grid, s));
+  return AGMM_OK;
+}
+
+int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* out,
+                        void* hip_stream) {
+  if (!h || !h->ar_D) return AGMM_ERR_INVALID_ARG;
+  const agmm_desc& d = h->desc;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != h->cfg.device) return AGMM_ERR_WRONG_DEVICE;
+  const int64_t c_bytes = d.M * d.N * 4, o_bytes = d.M * d.N * 2;
+  if ((c_bytes > 0 && (!C || !out)) || misaligned(C) || misaligned(out) || misaligned(bias))
+    return AGMM_ERR_INVALID_ARG;
+  if (overlaps(out, o_bytes, C, c_bytes) || overlaps(out, o_bytes, bias, d.N * 2))
+    return AGMM_ERR_INVALID_ARG;
+  AGMM_HIP(agmm::launch_ar_finalize(C, static_cast<const uint16_t*>(bias),
+                                    static_cast<uint16_t*>(out), d.M, d.N, d.dtype,
+                                    reinterpret_cast<hipStream_t>(hip_stream)));
+  return AGMM_OK;
 }
 
 int ag_matmul_debug_query(agmm_handle* h, int what, void* dst, size_t bytes) {

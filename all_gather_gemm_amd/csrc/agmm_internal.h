@@ -65,12 +65,21 @@ struct KParams {
   int32_t debug, trace_cap;
   uint32_t spin_limit;
   int32_t skip_unit;
+  // GEMM + all-reduce (atomics): this rank's partial tiles are added into the ar_D result
+  // buffers (fp32 [M][N]) instead of being stored
+  int32_t ar_D, ar_rank;
+  float* ar_out[AGMM_MAX_SHARDS];
 };
 
 // Launchers (defined in agmm_kernels.hip). block_m selects the tile family.
 hipError_t launch_fused(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 hipError_t launch_gemm_only(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s);
+// The GEMM-only persistent kernel whose tiles are added (fp32 atomics) into p.ar_out[].
+hipError_t launch_gemm_ar(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
+// out[m][n] = RNE(C[m][n] + bias[n]) for the 16-bit type; N % 4 == 0.
+hipError_t launch_ar_finalize(const float* C, const uint16_t* bias, uint16_t* out, int64_t M,
+                              int64_t N, int dtype, hipStream_t s);
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
 hipError_t launch_fill32(uint32_t* dst, int64_t n, uint32_t v, hipStream_t s);
 // Resident workgroups per CU for the fused kernel of this family (occupancy query).

@@ -406,7 +406,7 @@ __device__ inline int grab(const KParams& p);
 // last adds all of them in piece order (so the sum does not depend on which piece ends
 // last) and runs the epilogue. is_last: an LDS word for that decision.
 //
-template <class T, int DT, bool A_KMAJOR, bool WAIT, bool ROW>
+template <class T, int DT, bool A_KMAJOR, bool WAIT, bool ROW, int EPI = 0>
 __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t_m, int t_n,
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
@@ -715,6 +715,67 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     if (!*is_last) return;
     parts = slots;
     finish_split = true;
+  }
+
+  // GEMM + all-reduce with atomics (ROCm/iris PR "Let's make Iris' All-reduce the best!", the
+  // atomics example): this rank's partial tile is added into every rank's fp32 result,
+  // starting with rank + 1's (the order that spreads a multi-GPU run over its peers).
+  // The accumulator layout gives a lane 4 columns of one row and the wave 32 rows, so an
+  // atomic issued from it would touch 32 cache lines; instead each wave passes its block
+  // through LDS 32 rows at a time and reads it back so that one instruction's lanes cover
+  // consecutive columns of one row (two 128-byte lines at WTN >= 64).
+  if constexpr (EPI == 1) {
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    constexpr int RS = T::WTN + 4;                   // padded row stride (floats)
+    constexpr int LPR = T::WTN < 64 ? T::WTN : 64;   // lanes per row on read-back
+    constexpr int RPI = 64 / LPR;                    // rows per read-back instruction
+    constexpr int CPL = T::WTN / LPR;                // read-back columns per lane and row
+    constexpr int NV = 32 * T::WTN / 64;             // read-back values per lane per block
+    constexpr int VG = NV < 16 ? NV : 16;            // values held per group
+    static_assert(kThreads / 64 * 32 * RS * 4 <= T::NS * T::STAGE * 16, "blocks fit the stages");
+    static_assert(NV % VG == 0, "whole groups");
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the stages
+    lds_f32* blk = reinterpret_cast<lds_f32*>(st.s(0)) + wave * (32 * RS);
+    const int rl = lane / LPR, cl = lane % LPR;
+#pragma unroll
+    for (int fm = 0; fm < T::FM; ++fm) {
+#pragma unroll
+      for (int fn = 0; fn < T::FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = acc_read(acc[fm][fn], 4 * g + j);
+          *reinterpret_cast<lds_f32x4*>(blk + (lane & 31) * RS + fn * 32 + g * 8 + (lane >> 5) * 4) = v;
+        }
+      __syncthreads();
+      const int tr0 = wm * T::WTM + fm * 32;  // tile row of the block's first row
+      const int tc0 = wn * T::WTN;            // tile column of its first column
+#pragma unroll
+      for (int v0 = 0; v0 < NV; v0 += VG) {
+        float x[VG];
+#pragma unroll
+        for (int k = 0; k < VG; ++k) {
+          const int v = v0 + k;
+          x[k] = blk[((v / CPL) * RPI + rl) * RS + (v % CPL) * LPR + cl];
+        }
+        for (int i = 0; i < p.ar_D; ++i) {
+          float* dst = p.ar_out[(p.ar_rank + 1 + i) % p.ar_D];
+#pragma unroll
+          for (int k = 0; k < VG; ++k) {
+            const int v = v0 + k;
+            const int tr = tr0 + (v / CPL) * RPI + rl, tc = tc0 + (v % CPL) * LPR + cl;
+            if (tr < rows_valid && tc < cols_valid)
+              __hip_atomic_fetch_add(dst + (m0 + tr) * p.N + n0 + tc, x[k], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+      __syncthreads();  // the block is read before the next one overwrites it
+    }
+    return;
   }
 
   // Epilogue through LDS (all stages are free: every DMA has landed and the last barrier
@@ -1081,7 +1142,7 @@ __device__ inline int grab(const KParams& p) {
 // at its start for all of its k-groups and its K loop has no waits (used when every fetch
 // unit has a fetcher of its own, so the whole fetch is one pass); otherwise the K loop
 // waits for each k-group as it gets there.
-template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW>
+template <int BM, int DT, bool FUSED, bool LAYOUT_K, bool ROW, int EPI = 0>
 __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   using T = Tile<BM>;
   // the stages, contiguous: a stage's base is then arithmetic on the first one's address,
@@ -1120,7 +1181,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false, false>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, false, false, EPI>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else if constexpr (LAYOUT_K) {
       gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
     } else {
@@ -1222,7 +1283,60 @@ hipError_t occ_t(int* per_cu) {
   return hipSuccess;
 }
 
+// out[m][n] = RNE(C[m][n] + bias[n]): four consecutive outputs per thread and step.
+template <int DT>
+__global__ __launch_bounds__(256) void ar_finalize(const float* C, const uint16_t* bias,
+                                                   uint16_t* out, int64_t M, int64_t N) {
+  const int64_t groups = M * N / 4;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < groups;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t e = q * 4, n = e % N;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(C + e);
+    float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (bias) x[j] += Num<DT>::from_bits(bias[n + j]);
+      o[j] = Num<DT>::to_bits(x[j]);
+    }
+    *reinterpret_cast<u32x2*>(out + e) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_ar(const KParams& p, int dtype, int block_m, int grid, hipStream_t s) {
+  const bool bf = dtype == AGMM_BF16;
+  switch (block_m) {
+#define AGMM_AR_CASE(B)                                                                          \
+  case B:                                                                                        \
+    if (bf)                                                                                      \
+      hipLaunchKernelGGL((agmm_persistent<B, AGMM_BF16, false, true, false, 1>), dim3(grid),     \
+                         dim3(kThreads), 0, s, p);                                               \
+    else                                                                                         \
+      hipLaunchKernelGGL((agmm_persistent<B, AGMM_F16, false, true, false, 1>), dim3(grid),      \
+                         dim3(kThreads), 0, s, p);                                               \
+    break;
+    AGMM_AR_CASE(256)
+    AGMM_AR_CASE(128)
+    AGMM_AR_CASE(64)
+#undef AGMM_AR_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ar_finalize(const float* C, const uint16_t* bias, uint16_t* out, int64_t M,
+                              int64_t N, int dtype, hipStream_t s) {
+  const int64_t groups = M * N / 4;
+  if (groups <= 0) return hipSuccess;
+  const int blocks = (int)min((int64_t)2048, (groups + 255) / 256);
+  if (dtype == AGMM_BF16)
+    hipLaunchKernelGGL(ar_finalize<AGMM_BF16>, dim3(blocks), dim3(256), 0, s, C, bias, out, M, N);
+  else
+    hipLaunchKernelGGL(ar_finalize<AGMM_F16>, dim3(blocks), dim3(256), 0, s, C, bias, out, M, N);
+  return hipGetLastError();
+}
 
 hipError_t launch_fused(const KParams& p, int dtype, int block_m, int grid, hipStream_t s) {
   return launch_any<true>(p, dtype, block_m, grid, s);

@@ -142,6 +142,52 @@ def gather_variant(w, dev, steps, warmup, torch, A):
     return res
 
 
+def gemm_allreduce_variant(w, steps, warmup, torch, A):
+    """One rank's share of GEMM + all-reduce (atomics) on the workload's output shape: A_r
+    [M, K/D] @ B_r [K/D, N] added in fp32 into the D result buffers with device atomics.
+    Median ms of that share and of the plain GEMM of the same shape (16-bit output, no
+    atomics), interleaved on one stream; TFLOP/s of the share and its atomic-add rate
+    (D * M * N fp32 adds per share), and the ms of the finalize pass (one buffer to 16 bits).
+    """
+    D, M, N, Kl = w.D, w.M, w.N, w.K // w.D
+    tdt = w.torch_dtype()
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn((M, Kl), generator=g, device="cuda").div_(Kl ** 0.5).to(tdt)
+    b = torch.randn((Kl, N), generator=g, device="cuda").to(tdt)
+    C = [torch.zeros((M, N), dtype=torch.float32, device="cuda") for _ in range(D)]
+    out = torch.empty((M, N), dtype=tdt, device="cuda")
+    ar = A.GemmAllReduce(D, w.rank, M, N, Kl, w.dtype)
+    plain = A.AgMatmul(1, M, N, Kl, dtype=w.dtype, algo="baseline")
+    runs = {"share_ms": lambda: ar.run(a, b, C, check=False),
+            "plain_gemm_ms": lambda: plain.run([a], b, None, out=out, check=False),
+            "finalize_ms": lambda: ar.finalize(C[0], None, out=out)}
+    for _ in range(warmup):
+        for f in runs.values():
+            f()
+    torch.cuda.synchronize()
+    ev = {k: [] for k in runs}
+    keys = list(runs)
+    for i in range(steps):
+        for k in (keys if i % 2 == 0 else keys[::-1]):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            runs[k]()
+            e1.record()
+            ev[k].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {"D": D, "M": M, "N": N, "K_local": Kl, "dtype": w.dtype}
+    for k in keys:
+        res[k] = round(statistics.median(e0.elapsed_time(e1) for e0, e1 in ev[k]), 5)
+    res["share_tflops"] = round(tflops(M, N, Kl, res["share_ms"] * 1e-3), 1)
+    res["atomic_adds_per_s"] = round(D * M * N / (res["share_ms"] * 1e-3), 0)
+    res["atomic_GBps"] = round(D * M * N * 4 / (res["share_ms"] * 1e-3) / 1e9, 1)
+    ar.close()
+    plain.close()
+    del a, b, C, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def yardstick_matmul(w, dev, steps, warmup, torch):
     """torch.matmul on a pre-gathered A (library GEMM, context only)."""
     Ag = torch.cat(dev.shards, 0)
@@ -352,6 +398,7 @@ def main():
         res["yardstick_torch_matmul_pregathered"] = {
             "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}
         res["gather_a_variant"] = gather_variant(w, r["dev"], args.steps, args.warmup, torch, A)
+        res["gemm_allreduce_variant"] = gemm_allreduce_variant(w, args.steps, args.warmup, torch, A)
         # the host stream pipeline (chunked copy + GEMM-only kernels rotating over 4
         # streams), from the same interleaved runs
         pv = {f"chunks_{cfgs[n]['pipeline_chunks']}_median_ms": round(med[n], 5)

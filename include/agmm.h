@@ -192,6 +192,33 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream);
 
+/* ---- GEMM + all-reduce, atomics variant: one rank's share ----
+ * The mirror op of the all-gather (ROCm/iris PR "Let's make Iris' All-reduce the best!": a
+ * persistent GEMM whose ranks accumulate into each other's results with atomic adds). Rank
+ * r of D holds A_r = A[:, K_r] and B_r = B[K_r, :] (K_r its slice of the inner dimension);
+ * the op leaves C = sum_r A_r @ B_r = A @ B in every rank's fp32 result buffer.
+ *
+ * ag_gemm_ar_create: a handle for rank `rank` of `D` (1 <= D <= AGMM_MAX_SHARDS), output
+ *   [M, N], local inner dimension K_local (the same shape rules as ag_matmul_create, with
+ *   K = K_local), 16-bit type `dtype`, block_m 0 (auto), 64, 128 or 256. Destroy it with
+ *   ag_matmul_destroy. ag_matmul_run and ag_matmul_run_gather refuse it.
+ * ag_gemm_ar_run: enqueues this rank's share on `hip_stream`: A_local @ B_local computed in
+ *   fp32 and added, element by element, into each of the D buffers C[0..D-1] (fp32 [M, N]
+ *   row-major, device, 16-byte aligned, disjoint from each other and from the inputs), rank
+ *   + 1's first. The caller zeroes the buffers before the first rank adds into them; once
+ *   all D ranks' shares have run, each holds C. Additions from concurrent shares are
+ *   atomic; their order, and so the last bits of C, then depend on timing.
+ *     A_local: device [M, K_local] row-major; B_local: device [K_local, N] row-major.
+ * ag_gemm_ar_finalize: out[m][n] = RNE(C[m][n] + bias[n]) in the handle's 16-bit type (bias
+ *   [N] 16-bit, or NULL); out [M, N] row-major, not overlapping C.
+ * Return codes as for ag_matmul_run. */
+int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, int dtype,
+                      int block_m, agmm_handle** out_handle);
+int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, float* const* C,
+                   void* hip_stream);
+int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* out,
+                        void* hip_stream);
+
 /* Synchronizes the handle's device and frees its workspace (and a pipelined handle's
  * streams and events). NULL-safe. */
 int ag_matmul_destroy(agmm_handle* h);

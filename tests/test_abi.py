@@ -28,7 +28,7 @@ def header_functions():
     with open(os.path.join(ROOT, "include", "agmm.h")) as fh:
         text = fh.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ag_matmul_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ag_(?:matmul|gemm_ar)_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(A):
