@@ -24,13 +24,14 @@ CASES = [
     (4, 384, 392, 200, "f16", 64),
     (8, 1024, 1024, 128, "bf16", 0),
     (3, 200, 136, 72, "f16", 256),
+    (2, 130, 72, 0, "bf16", 0),      # K_local = 0: the result is zero (+ bias)
 ]
 
 
 def _parts(D, M, N, Kl, dt, seed):
     g = torch.Generator().manual_seed(seed)
     tdt = torch.float16 if dt == "f16" else torch.bfloat16
-    K = D * Kl
+    K = max(D * Kl, 1)
     A = [(torch.randn(M, Kl, generator=g) / K ** 0.5).to(tdt) for _ in range(D)]
     B = [(torch.randn(Kl, N, generator=g) / K ** 0.5).to(tdt) for _ in range(D)]
     bias = torch.rand(N, generator=g).mul(2).sub(1).to(tdt)
@@ -95,6 +96,20 @@ def test_allreduce_concurrent_shares():
         assert (np.abs(c.cpu().numpy().astype(np.float64) - Cref) <= bound).all()
     for h in hs:
         h.close()
+
+
+def test_allreduce_empty_output():
+    """M = 0: nothing to add and nothing to round; both calls succeed and launch nothing."""
+    import all_gather_gemm_amd as AG
+    g = AG.GemmAllReduce(2, 1, 0, 64, 64)
+    A = torch.zeros((1, 64), dtype=torch.float16, device="cuda")
+    C = [torch.zeros((1, 64), dtype=torch.float32, device="cuda") for _ in range(2)]
+    assert g.run(A, A, C) == 0
+    out = torch.full((1, 64), 7.0, dtype=torch.float16, device="cuda")
+    assert g.finalize(C[0], None, out=out) is out
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+    g.close()
 
 
 def test_allreduce_refusals():
