@@ -38,7 +38,7 @@ EXPORTED = [
     "ag_matmul_workspace_bytes", "ag_matmul_strerror", "ag_matmul_last_hip_error",
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
-    "ag_gemm_ar_finalize",
+    "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
 ]
 
 
@@ -108,6 +108,10 @@ def _load():
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
     lib.ag_gemm_ar_run.argtypes = [vp, vp, vp, ctypes.POINTER(vp), vp]
     lib.ag_gemm_ar_finalize.argtypes = [vp, vp, vp, vp, vp]
+    lib.ag_gemm_ar_flags_create.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                            ctypes.POINTER(vp)]
+    lib.ag_gemm_ar_flags_run.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.ag_matmul_destroy.argtypes = [vp]
     lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
@@ -426,4 +430,49 @@ class GemmAllReduce:
                                      ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
         if rc != AGMM_OK:
             raise AgmmError(rc, "ag_gemm_ar_finalize")
+        return out
+
+
+class GemmAllReduceFlags:
+    """GEMM + all-reduce with a ready flag per tile, every rank's share in one launch:
+    run(A_parts, B_parts, bias) returns RNE(sum_r A_parts[r] @ B_parts[r] + bias)."""
+
+    def __init__(self, D: int, M: int, N: int, K_local: int, dtype="f16", block_m: int = 0):
+        h = ctypes.c_void_p()
+        rc = lib.ag_gemm_ar_flags_create(D, M, N, K_local, {"f16": F16, "bf16": BF16}[dtype],
+                                         block_m, ctypes.byref(h))
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_gemm_ar_flags_create")
+        self.handle, self.D, self.M, self.N, self.K, self.dtype = h.value, D, M, N, K_local, dtype
+        self.config = ag_matmul_get_config(self.handle)
+
+    def close(self):
+        if self.handle:
+            ag_matmul_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, A_parts, B_parts, bias=None, out=None, stream=None, check: bool = True):
+        import torch
+        if len(A_parts) != self.D or len(B_parts) != self.D:
+            raise ValueError(f"expected {self.D} A and B parts")
+        tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        for t in list(A_parts) + list(B_parts) + ([bias] if bias is not None else []):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors of the handle's type")
+        if out is None:
+            out = torch.empty((self.M, self.N), dtype=tdt, device=A_parts[0].device)
+        s = stream if stream is not None else torch.cuda.current_stream(out.device)
+        ap = (ctypes.c_void_p * self.D)(*[ctypes.c_void_p(t.data_ptr()) for t in A_parts])
+        bp = (ctypes.c_void_p * self.D)(*[ctypes.c_void_p(t.data_ptr()) for t in B_parts])
+        rc = lib.ag_gemm_ar_flags_run(ctypes.c_void_p(self.handle), ap, bp,
+                                      ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
+                                      ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+        if check and rc != AGMM_OK:
+            raise AgmmError(rc, "ag_gemm_ar_flags_run")
         return out

@@ -50,6 +50,15 @@ struct agmm_handle {
   int n_pstreams, n_events;  // created so far (destroy releases these)
   // GEMM + all-reduce handles (ag_gemm_ar_create): ranks and this rank; 0 otherwise
   int32_t ar_D, ar_rank;
+  // ag_gemm_ar_flags_create: every rank's share in one launch. A second device allocation
+  // holds the partial tiles [D][M][N] fp32, the flags [D][tiles] and the item list.
+  bool ar_flags_mode;
+  char* ar_ws;
+  float* ar_partials;
+  uint32_t* ar_flags;
+  uint32_t* ar_items;
+  int64_t ar_flags_n, ar_items_n;
+  uint32_t ar_epoch;
 };
 
 namespace {
@@ -577,6 +586,7 @@ int ag_matmul_destroy(agmm_handle* h) {
   hipError_t e = hipDeviceSynchronize();
   release_streams(h);
   if (e == hipSuccess) e = hipFree(h->ws);
+  if (e == hipSuccess && h->ar_ws) e = hipFree(h->ar_ws);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
     rc = AGMM_ERR_HIP;
@@ -796,7 +806,7 @@ int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, in
 
 int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, float* const* C,
                    void* hip_stream) {
-  if (!h || !h->ar_D || !C) return AGMM_ERR_INVALID_ARG;
+  if (!h || !h->ar_D || h->ar_flags_mode || !C) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
@@ -837,7 +847,7 @@ int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, flo
 
 int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* out,
                         void* hip_stream) {
-  if (!h || !h->ar_D) return AGMM_ERR_INVALID_ARG;
+  if (!h || !h->ar_D || h->ar_flags_mode) return AGMM_ERR_INVALID_ARG;
   const agmm_desc& d = h->desc;
   int cur = 0;
   AGMM_HIP(hipGetDevice(&cur));
@@ -850,6 +860,102 @@ int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* 
   AGMM_HIP(agmm::launch_ar_finalize(C, static_cast<const uint16_t*>(bias),
                                     static_cast<uint16_t*>(out), d.M, d.N, d.dtype,
                                     reinterpret_cast<hipStream_t>(hip_stream)));
+  return AGMM_OK;
+}
+
+int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dtype,
+                            int block_m, agmm_handle** out_handle) {
+  if (!out_handle) return AGMM_ERR_INVALID_ARG;
+  *out_handle = nullptr;
+  if (D < 1 || D > AGMM_MAX_SHARDS) return AGMM_ERR_INVALID_ARG;
+  agmm_handle* h = nullptr;
+  int rc = ag_gemm_ar_create(D, 0, M, N, K_local, dtype, block_m, &h);
+  if (rc != AGMM_OK) return rc;
+  const agmm_config& c = h->cfg;
+  const int64_t tiles = (int64_t)c.T_m * c.T_n;
+  // Item order: tile by tile, its D producers; tile t's reducer follows the producers of
+  // tile t + lag, lag = the tiles whose producers one round of the grid covers, so that a
+  // reducer mostly finds its flags set.
+  const int64_t grid_max = std::max<int64_t>(1, c.num_cus);
+  const int64_t lag = (grid_max + D - 1) / D;
+  std::vector<uint32_t> items;
+  items.reserve((size_t)(tiles * (D + 1)));
+  for (int64_t t = 0; t < tiles; ++t) {
+    for (int r = 0; r < D; ++r) items.push_back(((uint32_t)r << 24) | (uint32_t)t);
+    if (t >= lag) items.push_back(agmm::kArReduceItem | (uint32_t)(t - lag));
+  }
+  for (int64_t t = std::max<int64_t>(0, tiles - lag); t < tiles; ++t)
+    items.push_back(agmm::kArReduceItem | (uint32_t)t);
+  h->ar_flags_mode = true;
+  h->ar_items_n = (int64_t)items.size();
+  h->ar_flags_n = D * tiles;
+  const int64_t part_b = align256((int64_t)D * M * N * 4);
+  const int64_t flag_b = align256(h->ar_flags_n * 4), item_b = align256(h->ar_items_n * 4);
+  if (part_b + flag_b + item_b > 0) {
+    if (hipMalloc(&h->ar_ws, (size_t)(part_b + flag_b + item_b)) != hipSuccess) {
+      (void)hipGetLastError();
+      ag_matmul_destroy(h);
+      return AGMM_ERR_OOM;
+    }
+    h->ar_partials = reinterpret_cast<float*>(h->ar_ws);
+    h->ar_flags = reinterpret_cast<uint32_t*>(h->ar_ws + part_b);
+    h->ar_items = reinterpret_cast<uint32_t*>(h->ar_ws + part_b + flag_b);
+    hipError_t e = hipMemset(h->ar_flags, 0, (size_t)flag_b);
+    if (e == hipSuccess && !items.empty())
+      e = hipMemcpy(h->ar_items, items.data(), items.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      g_last_hip = (int)e;
+      ag_matmul_destroy(h);
+      return AGMM_ERR_HIP;
+    }
+  }
+  *out_handle = h;
+  return AGMM_OK;
+}
+
+int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void* const* B_parts,
+                         const void* bias, void* out, void* hip_stream) {
+  if (!h || !h->ar_flags_mode || !A_parts || !B_parts) return AGMM_ERR_INVALID_ARG;
+  if (h->poisoned) return AGMM_ERR_POISONED;
+  const agmm_desc& d = h->desc;
+  const agmm_config& c = h->cfg;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != c.device) return AGMM_ERR_WRONG_DEVICE;
+  const int D = h->ar_D;
+  const int64_t a_bytes = d.M * d.K * 2, b_bytes = d.K * d.N * 2, o_bytes = d.M * d.N * 2;
+  if ((o_bytes > 0 && !out) || misaligned(out) || misaligned(bias)) return AGMM_ERR_INVALID_ARG;
+  if (overlaps(out, o_bytes, bias, d.N * 2)) return AGMM_ERR_INVALID_ARG;
+  for (int r = 0; r < D; ++r) {
+    if ((a_bytes > 0 && !A_parts[r]) || misaligned(A_parts[r])) return AGMM_ERR_INVALID_ARG;
+    if ((b_bytes > 0 && !B_parts[r]) || misaligned(B_parts[r])) return AGMM_ERR_INVALID_ARG;
+    if (overlaps(out, o_bytes, A_parts[r], a_bytes) || overlaps(out, o_bytes, B_parts[r], b_bytes))
+      return AGMM_ERR_INVALID_ARG;
+  }
+  if (c.num_tiles == 0) return AGMM_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if (h->ar_epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
+    AGMM_HIP(agmm::launch_fill32(h->ar_flags, h->ar_flags_n, 0u, s));
+    h->ar_epoch = 0;
+  }
+  const uint32_t epoch = ++h->ar_epoch;
+  KParams p = run_params(h, A_parts, nullptr, bias, out, h->staging, epoch);
+  for (int r = 0; r < D; ++r) {
+    p.shards[r] = static_cast<const uint16_t*>(A_parts[r]);
+    p.ar_B[r] = static_cast<const uint16_t*>(B_parts[r]);
+  }
+  p.F = 0;
+  p.staged_kmajor = 1;
+  p.debug = 0;
+  p.trace_cap = 0;
+  p.ar_D = D;
+  p.partials = h->ar_partials;
+  p.flags = h->ar_flags;
+  p.qtiles = h->ar_items;
+  for (int x = 0; x < agmm::kQueueSlots; ++x) p.qoff[x] = p.qlen[x] = 0;
+  p.qlen[0] = (int32_t)h->ar_items_n;
+  const int grid = (int)std::min<int64_t>(c.num_cus, h->ar_items_n);
+  AGMM_HIP(agmm::launch_ar_flags(p, d.dtype, c.block_m, grid, s));
   return AGMM_OK;
 }
 

@@ -23,6 +23,9 @@ constexpr int kQueueSlots = kQueues + 1;
 // Queue entry: bits 0-23 tile id (position of its m-tile in GEMM order * T_n + n-tile),
 // bits 24-27 piece, bits 28-31 pieces - 1 (0: the tile is not split).
 constexpr uint32_t kItemTileMask = 0x00ffffffu;
+// GEMM + all-reduce with per-tile flags: an item with this bit reduces its tile (else bits
+// 24..29 name the rank whose partial tile it computes)
+constexpr uint32_t kArReduceItem = 1u << 30;
 constexpr int kMaxSplit = 4;
 
 // Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
@@ -69,6 +72,9 @@ struct KParams {
   // buffers (fp32 [M][N]) instead of being stored
   int32_t ar_D, ar_rank;
   float* ar_out[AGMM_MAX_SHARDS];
+  // GEMM + all-reduce with per-tile flags: rank r's B slice ([K][N], K = its inner
+  // dimension); its A slice is shards[r] ([M][K])
+  const uint16_t* ar_B[AGMM_MAX_SHARDS];
 };
 
 // Launchers (defined in agmm_kernels.hip). block_m selects the tile family.
@@ -77,6 +83,9 @@ hipError_t launch_gemm_only(const KParams& p, int dtype, int block_m, int grid, 
 hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s);
 // The GEMM-only persistent kernel whose tiles are added (fp32 atomics) into p.ar_out[].
 hipError_t launch_gemm_ar(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
+// GEMM + all-reduce with per-tile flags, every rank's share in one launch: items in
+// p.qtiles (queue 0), partial tiles in p.partials, flags in p.flags ([D][tiles]).
+hipError_t launch_ar_flags(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 // out[m][n] = RNE(C[m][n] + bias[n]) for the 16-bit type; N % 4 == 0.
 hipError_t launch_ar_finalize(const float* C, const uint16_t* bias, uint16_t* out, int64_t M,
                               int64_t N, int dtype, hipStream_t s);

@@ -411,7 +411,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
                                                          int tid_in, Tracer& tr, int* next_tile,
-                                                         int* is_last) {
+                                                         int* is_last, int src = 0) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   // this piece's K-tiles [kt_lo, kt_lo + KT)
   const int KT_all = (int)((p.K + BK - 1) / BK);
@@ -481,7 +481,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   const uint16_t* abase;
   int64_t lda, a_bytes;
   if (!staged) {
-    abase = p.shards[p.rank] + (m0 - (int64_t)p.rank * p.M_s) * p.K;
+    abase = p.shards[EPI == 2 ? src : p.rank] + (m0 - (int64_t)p.rank * p.M_s) * p.K;
     lda = p.K;
     a_bytes = (p.M_s * p.K - (m0 - (int64_t)p.rank * p.M_s) * p.K) * 2;
   } else if (A_KMAJOR) {
@@ -495,7 +495,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   }
   // step of the A base per K-tile: BK columns (K-major) or BK rows (m_contiguous)
   const int64_t a_step = A_KMAJOR ? (int64_t)BK : (int64_t)BK * lda;
-  const uint16_t* bbase = p.B + n0;
+  const uint16_t* bbase = (EPI == 2 ? p.ar_B[src] : p.B) + n0;
   int64_t b_bytes = (p.K * p.N - n0) * 2;
   const int64_t b_step = (int64_t)BK * p.N;
   // the operand bases start at K-tile kt_lo
@@ -724,7 +724,10 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   // atomic issued from it would touch 32 cache lines; instead each wave passes its block
   // through LDS 32 rows at a time and reads it back so that one instruction's lanes cover
   // consecutive columns of one row (two 128-byte lines at WTN >= 64).
-  if constexpr (EPI == 1) {
+  // EPI 2 (the per-tile flag variant): the same read-back, with plain stores of the fp32
+  // tile into rank src's partial buffer p.partials + src * M * N ([M][N]); the caller
+  // publishes it.
+  if constexpr (EPI == 1 || EPI == 2) {
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     constexpr int RS = T::WTN + 4;                   // padded row stride (floats)
@@ -761,15 +764,25 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
           const int v = v0 + k;
           x[k] = blk[((v / CPL) * RPI + rl) * RS + (v % CPL) * LPR + cl];
         }
-        for (int i = 0; i < p.ar_D; ++i) {
-          float* dst = p.ar_out[(p.ar_rank + 1 + i) % p.ar_D];
+        if constexpr (EPI == 1) {
+          for (int i = 0; i < p.ar_D; ++i) {
+            float* dst = p.ar_out[(p.ar_rank + 1 + i) % p.ar_D];
+#pragma unroll
+            for (int k = 0; k < VG; ++k) {
+              const int v = v0 + k;
+              const int tr = tr0 + (v / CPL) * RPI + rl, tc = tc0 + (v % CPL) * LPR + cl;
+              if (tr < rows_valid && tc < cols_valid)
+                __hip_atomic_fetch_add(dst + (m0 + tr) * p.N + n0 + tc, x[k], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        } else {
+          float* dst = p.partials + (int64_t)src * p.M * p.N;
 #pragma unroll
           for (int k = 0; k < VG; ++k) {
             const int v = v0 + k;
             const int tr = tr0 + (v / CPL) * RPI + rl, tc = tc0 + (v % CPL) * LPR + cl;
-            if (tr < rows_valid && tc < cols_valid)
-              __hip_atomic_fetch_add(dst + (m0 + tr) * p.N + n0 + tc, x[k], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            if (tr < rows_valid && tc < cols_valid) dst[(m0 + tr) * p.N + n0 + tc] = x[k];
           }
         }
       }
@@ -1208,6 +1221,98 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   }
 }
 
+// GEMM + all-reduce with per-tile flags (ROCm/iris PR "Let's make Iris' All-reduce the
+// best!", its one-shot variant with a ready flag per tile), every rank's share in one
+// launch. Items, in the order of p.qtiles (queue 0 only): producer (r << 24 | tile)
+// computes rank r's partial tile A_r @ B_r into p.partials + r * M * N and publishes flag
+// r * tiles + tile with the run's epoch; reducer (kArReduceItem | tile) waits for the D flags
+// of its tile and writes RNE(sum over r in rank order + bias). A reducer comes after its
+// tile's D producers in the claim order, and producers never wait, so every wait ends.
+
+template <class T, int DT>
+__device__ __attribute__((always_inline)) void reduce_tile(const KParams& p, int t_m, int t_n,
+                                                           int tile, int tid, Tracer& tr) {
+  constexpr int BM = T::BM, BN = T::BN;
+  const int64_t tiles = (int64_t)p.T_m * p.T_n;
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
+    for (int r = 0; r < p.ar_D; ++r) poll_flag(p, r * tiles + tile, p.epoch, tr);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  const int64_t m0 = (int64_t)t_m * BM, n0 = (int64_t)t_n * BN, MN = p.M * p.N;
+  const int rows = (int)min((int64_t)BM, p.M - m0), cols = (int)min((int64_t)BN, p.N - n0);
+  // four consecutive columns per thread and step (N and so cols are multiples of 8: a group
+  // is wholly inside or outside); up to 8 ranks' loads in flight before their adds
+  for (int e = tid * 4; e < BM * BN; e += kThreads * 4) {
+    const int row = e / BN, col = e % BN;
+    if (row >= rows || col >= cols) continue;
+    const float* src = p.partials + (m0 + row) * p.N + n0 + col;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+    for (int r0 = 1; r0 < p.ar_D; r0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < p.ar_D) v[j] = *reinterpret_cast<const f32x4*>(src + (r0 + j) * MN);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < p.ar_D) acc += v[j];
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x = acc[j];
+      if (p.bias) x += Num<DT>::from_bits(p.bias[n0 + col + j]);
+      o[j] = Num<DT>::to_bits(x);
+    }
+    *reinterpret_cast<u32x2*>(p.out + (m0 + row) * p.N + n0 + col) =
+        u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+  }
+}
+
+template <int BM, int DT>
+__global__ __launch_bounds__(kThreads) void agmm_ar_flags(KParams p) {
+  using T = Tile<BM>;
+  __shared__ u32x4 lds_stages[T::NS * T::STAGE];
+  __shared__ u32x2 s_bias[T::BN / 4];
+  const Stages<T> st{(lds_u32x4*)lds_stages, (uint32_t)(size_t)(lds_void*)lds_stages};
+  __shared__ int s_next, s_last;
+  const int tid = threadIdx.x;
+  Tracer tr{nullptr, 0u, 0u, false};
+  const int64_t tiles = (int64_t)p.T_m * p.T_n;
+  if (tid == 0) s_next = grab(p);
+  __syncthreads();
+  int q = __builtin_amdgcn_readfirstlane(s_next);
+  while (q >= 0) {
+    __syncthreads();  // everyone has read s_next
+    const int tile = (int)((uint32_t)q & kItemTileMask);
+    const int t_m = tile / p.T_n, t_n = tile - t_m * p.T_n;
+    if (((uint32_t)q & kArReduceItem) == 0u) {
+      const int r = (int)(((uint32_t)q >> 24) & 63u);
+      gemm_tile<T, DT, true, false, false, 2>(p, t_m, t_n, 0, 1, false, st, s_bias, tid, tr,
+                                              &s_next, &s_last, r);
+      wait_vmcnt<0>();  // this thread's stores of the partial tile are done
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(p.flags + r * tiles + tile, p.epoch, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      reduce_tile<T, DT>(p, t_m, t_n, tile, tid, tr);
+      if (tid == 0) s_next = grab(p);
+    }
+    __syncthreads();
+    q = __builtin_amdgcn_readfirstlane(s_next);
+  }
+  if (tid == 0) {
+    const uint32_t old = atomicAdd(p.ctr + CTR_DONE, 1u);
+    if (old == gridDim.x - 1) {  // last workgroup out resets the queues for the next run
+      for (int x = 0; x < kQueueSlots; ++x)
+        __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Baseline copy: every staged unit into k_contiguous staging, no flags.
 template <int BM>
 __global__ __launch_bounds__(kThreads) void agmm_copy(KParams p) {
@@ -1322,6 +1427,26 @@ hipError_t launch_gemm_ar(const KParams& p, int dtype, int block_m, int grid, hi
     AGMM_AR_CASE(64)
 #undef AGMM_AR_CASE
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ar_flags(const KParams& p, int dtype, int block_m, int grid, hipStream_t s) {
+  const bool bf = dtype == AGMM_BF16;
+  switch (block_m) {
+#define AGMM_ARF_CASE(B)                                                                    \
+  case B:                                                                                   \
+    if (bf)                                                                                 \
+      hipLaunchKernelGGL((agmm_ar_flags<B, AGMM_BF16>), dim3(grid), dim3(kThreads), 0, s, p); \
+    else                                                                                    \
+      hipLaunchKernelGGL((agmm_ar_flags<B, AGMM_F16>), dim3(grid), dim3(kThreads), 0, s, p);  \
+    break;
+    AGMM_ARF_CASE(256)
+    AGMM_ARF_CASE(128)
+    AGMM_ARF_CASE(64)
+#undef AGMM_ARF_CASE
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -219,6 +219,28 @@ int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, flo
 int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* out,
                         void* hip_stream);
 
+/* GEMM + all-reduce with a ready flag per tile (ROCm/iris PR "Let's make Iris' All-reduce
+ * the best!", the one-shot variant with per-tile locks): every rank's share in one launch.
+ * Rank r's workgroups store their partial tile A_r @ B_r (fp32) into a partial buffer of
+ * the handle's and publish the tile's flag for r (release); the tile's reducer waits for
+ * the D flags (acquire) and writes out = RNE(sum of the D partials in rank order + bias).
+ * The result is deterministic: it does not depend on timing.
+ *
+ * ag_gemm_ar_flags_create: D ranks (1 <= D <= AGMM_MAX_SHARDS), output [M, N], inner
+ *   dimension K_local per rank (shape rules as ag_matmul_create with K = K_local), 16-bit
+ *   `dtype`, block_m 0 (auto), 64, 128 or 256. Allocates D * M * N * 4 bytes of partial
+ *   tiles besides the usual workspace; AGMM_ERR_OOM if that fails. Destroy it with
+ *   ag_matmul_destroy; the other run entry points refuse it.
+ * ag_gemm_ar_flags_run: enqueues the op on `hip_stream`. A_parts[r]: device [M, K_local]
+ *   row-major; B_parts[r]: device [K_local, N] row-major (r < D); bias [N] 16-bit or NULL;
+ *   out [M, N] 16-bit row-major, not overlapping any input. All 16-byte aligned. Runs of
+ *   one handle on several streams at once race on its partial buffer and flags.
+ * Return codes as for ag_matmul_run. */
+int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dtype,
+                            int block_m, agmm_handle** out_handle);
+int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void* const* B_parts,
+                         const void* bias, void* out, void* hip_stream);
+
 /* Synchronizes the handle's device and frees its workspace (and a pipelined handle's
  * streams and events). NULL-safe. */
 int ag_matmul_destroy(agmm_handle* h);

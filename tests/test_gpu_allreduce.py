@@ -131,3 +131,58 @@ def test_allreduce_refusals():
     torch.cuda.synchronize()
     g.close()
     plain.close()
+
+
+FLAG_CASES = CASES + [(2, 2048, 2048, 256, "f16", 128)]   # more tiles than the reducer lag
+
+
+@pytest.mark.parametrize("D,M,N,Kl,dt,bm", FLAG_CASES)
+def test_allreduce_flags_matches_oracle_and_atomics(D, M, N, Kl, dt, bm):
+    """The per-tile flag variant (every rank's share in one launch): within the 16-bit
+    tolerance of the oracle, the same bits on a second run, and bit-identical to the atomics
+    variant's shares run in rank order and finalized (both add the same fp32 partial tiles
+    in rank order, then the bias, then round once)."""
+    import all_gather_gemm_amd as AG
+    print(f"case ar-flags D={D} {M}x{N}x{Kl} {dt} bm={bm}", flush=True)
+    A, B, bias = _parts(D, M, N, Kl, dt, 900 + D)
+    Ad, Bd, bd = [a.cuda() for a in A], [b.cuda() for b in B], bias.cuda()
+    h = AG.GemmAllReduceFlags(D, M, N, Kl, dt, bm)
+    out = h.run(Ad, Bd, bd)
+    out2 = h.run(Ad, Bd, bd)
+    C = [torch.zeros((M, N), dtype=torch.float32, device="cuda") for _ in range(D)]
+    hs = [AG.GemmAllReduce(D, r, M, N, Kl, dt, bm) for r in range(D)]
+    for r in range(D):
+        hs[r].run(Ad[r], Bd[r], C)
+    fin = hs[0].finalize(C[(1) % D], bd)   # rank 0 adds into rank 1's buffer first; all equal
+    torch.cuda.synchronize()
+    Cref, _ = _reference(D, dt, A, B)
+    bdec = oracle.decode(dt, _bits(bias))
+    res = oracle.check(dt, out_bits(out), Cref + bdec[None, :])
+    assert res["bad"] == 0, res
+    assert np.array_equal(out_bits(out), out_bits(out2))
+    assert np.array_equal(out_bits(out), out_bits(fin))
+    for x in hs + [h]:
+        x.close()
+
+
+def test_allreduce_flags_refusals():
+    import all_gather_gemm_amd as AG
+    lib, vp = AG.lib, AG.ctypes.c_void_p
+    h = vp()
+    assert lib.ag_gemm_ar_flags_create(0, 64, 64, 64, 0, 0, AG.ctypes.byref(h)) == -1
+    g = AG.GemmAllReduceFlags(2, 64, 64, 64)
+    A = [torch.zeros((64, 64), dtype=torch.float16, device="cuda") for _ in range(2)]
+    s = torch.cuda.current_stream().cuda_stream
+    ap = (vp * 2)(*[vp(a.data_ptr()) for a in A])
+    assert lib.ag_gemm_ar_flags_run(vp(g.handle), ap, ap, None, vp(A[1].data_ptr()), vp(s)) == -1  # out = an input
+    C = [torch.zeros((64, 64), dtype=torch.float32, device="cuda") for _ in range(2)]
+    cp = (vp * 2)(*[vp(c.data_ptr()) for c in C])
+    assert lib.ag_gemm_ar_run(vp(g.handle), vp(A[0].data_ptr()), vp(A[0].data_ptr()), cp, vp(s)) == -1
+    assert lib.ag_gemm_ar_finalize(vp(g.handle), vp(C[0].data_ptr()), None, vp(A[0].data_ptr()), vp(s)) == -1
+    assert AG.ag_matmul_run(g.handle, [A[0].data_ptr()], A[0].data_ptr(), None, A[1].data_ptr(), s) == -1
+    plain = AG.GemmAllReduce(2, 0, 64, 64, 64)
+    out = torch.empty((64, 64), dtype=torch.float16, device="cuda")
+    assert lib.ag_gemm_ar_flags_run(vp(plain.handle), ap, ap, None, vp(out.data_ptr()), vp(s)) == -1
+    torch.cuda.synchronize()
+    g.close()
+    plain.close()
