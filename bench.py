@@ -148,6 +148,8 @@ def gemm_allreduce_variant(w, steps, warmup, torch, A):
     Median ms of that share and of the plain GEMM of the same shape (16-bit output, no
     atomics), interleaved on one stream; TFLOP/s of the share and its atomic-add rate
     (D * M * N fp32 adds per share), and the ms of the finalize pass (one buffer to 16 bits).
+    Also the per-tile flag variant, all D ranks' shares in one launch, against D shares of
+    the atomics variant plus a finalize (the same result on one GPU).
     """
     D, M, N, Kl = w.D, w.M, w.N, w.K // w.D
     tdt = w.torch_dtype()
@@ -158,9 +160,15 @@ def gemm_allreduce_variant(w, steps, warmup, torch, A):
     out = torch.empty((M, N), dtype=tdt, device="cuda")
     ar = A.GemmAllReduce(D, w.rank, M, N, Kl, w.dtype)
     plain = A.AgMatmul(1, M, N, Kl, dtype=w.dtype, algo="baseline")
+    # the per-tile flag variant: all D ranks' shares (distinct A_r, B_r) in one launch
+    a_parts = [a] + [torch.randn((M, Kl), generator=g, device="cuda").div_(Kl ** 0.5).to(tdt)
+                     for _ in range(D - 1)]
+    b_parts = [b] + [torch.randn((Kl, N), generator=g, device="cuda").to(tdt) for _ in range(D - 1)]
+    fl = A.GemmAllReduceFlags(D, M, N, Kl, w.dtype)
     runs = {"share_ms": lambda: ar.run(a, b, C, check=False),
             "plain_gemm_ms": lambda: plain.run([a], b, None, out=out, check=False),
-            "finalize_ms": lambda: ar.finalize(C[0], None, out=out)}
+            "finalize_ms": lambda: ar.finalize(C[0], None, out=out),
+            "flags_all_ranks_ms": lambda: fl.run(a_parts, b_parts, None, out=out, check=False)}
     for _ in range(warmup):
         for f in runs.values():
             f()
@@ -181,9 +189,12 @@ def gemm_allreduce_variant(w, steps, warmup, torch, A):
     res["share_tflops"] = round(tflops(M, N, Kl, res["share_ms"] * 1e-3), 1)
     res["atomic_adds_per_s"] = round(D * M * N / (res["share_ms"] * 1e-3), 0)
     res["atomic_GBps"] = round(D * M * N * 4 / (res["share_ms"] * 1e-3) / 1e9, 1)
+    res["flags_all_ranks_tflops"] = round(tflops(M, N, D * Kl, res["flags_all_ranks_ms"] * 1e-3), 1)
+    res["atomics_all_ranks_ms"] = round(D * res["share_ms"] + res["finalize_ms"], 5)
     ar.close()
     plain.close()
-    del a, b, C, out
+    fl.close()
+    del a, b, C, out, a_parts, b_parts
     torch.cuda.empty_cache()
     return res
 
