@@ -71,10 +71,14 @@ struct KParams {
   // GEMM + all-reduce (atomics): this rank's partial tiles are added into the ar_D result
   // buffers (fp32 [M][N]) instead of being stored
   int32_t ar_D, ar_rank;
-  float* ar_out[AGMM_MAX_SHARDS];
-  // GEMM + all-reduce with per-tile flags: rank r's B slice ([K][N], K = its inner
-  // dimension); its A slice is shards[r] ([M][K])
-  const uint16_t* ar_B[AGMM_MAX_SHARDS];
+  // The two all-reduce variants use one table, so that the struct, and with it every
+  // kernel's argument block, keeps its size: the atomics variant's result buffers, or the
+  // per-tile flag variant's B slices (rank r's [K][N], K its inner dimension; its A slice
+  // is shards[r], [M][K]).
+  union {
+    float* ar_out[AGMM_MAX_SHARDS];
+    const uint16_t* ar_B[AGMM_MAX_SHARDS];
+  };
 };
 
 // Launchers (defined in agmm_kernels.hip). block_m selects the tile family.
