@@ -39,6 +39,7 @@ EXPORTED = [
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
+    "ag_gemm_ar_flags_plan",
 ]
 
 
@@ -112,6 +113,11 @@ def _load():
                                             ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                             ctypes.POINTER(vp)]
     lib.ag_gemm_ar_flags_run.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
+    lib.ag_gemm_ar_flags_plan.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(agmm_config),
+                                          ctypes.POINTER(ctypes.c_uint32),
+                                          ctypes.POINTER(ctypes.c_int64)]
     lib.ag_matmul_destroy.argtypes = [vp]
     lib.ag_matmul_workspace_bytes.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_workspace_bytes.restype = ctypes.c_int64
@@ -476,3 +482,23 @@ class GemmAllReduceFlags:
         if check and rc != AGMM_OK:
             raise AgmmError(rc, "ag_gemm_ar_flags_run")
         return out
+
+
+def ag_gemm_ar_flags_plan(D: int, M: int, N: int, K_local: int, dtype="f16", block_m: int = 0,
+                          num_cus: int = 256):
+    """Host only: (config dict, item list) that a per-tile flag handle would use."""
+    import numpy as np
+    cfg = agmm_config()
+    n = ctypes.c_int64(0)
+    dt = {"f16": F16, "bf16": BF16}[dtype]
+    rc = lib.ag_gemm_ar_flags_plan(D, M, N, K_local, dt, block_m, num_cus, ctypes.byref(cfg),
+                                   None, ctypes.byref(n))
+    if rc != AGMM_OK:
+        raise AgmmError(rc, "ag_gemm_ar_flags_plan")
+    items = np.zeros(n.value, dtype=np.uint32)
+    rc = lib.ag_gemm_ar_flags_plan(D, M, N, K_local, dt, block_m, num_cus, None,
+                                   items.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                   ctypes.byref(n))
+    if rc != AGMM_OK:
+        raise AgmmError(rc, "ag_gemm_ar_flags_plan")
+    return cfg.as_dict(), items

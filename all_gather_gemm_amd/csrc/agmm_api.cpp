@@ -652,6 +652,36 @@ KParams run_params(agmm_handle* h, const void* const* shards, const void* B, con
   return p;
 }
 
+// GEMM + all-reduce with per-tile flags, the claim order: tile by tile, its D producers
+// (r << 24 | tile); tile t's reducer (kArReduceItem | t) follows the producers of tile
+// t + lag, lag = the tiles whose producers one round of the grid covers, so that a reducer
+// mostly finds its flags set. Every reducer comes after its tile's producers.
+std::vector<uint32_t> ar_flag_items(int D, int64_t tiles, int64_t num_cus) {
+  const int64_t lag = (std::max<int64_t>(1, num_cus) + D - 1) / D;
+  std::vector<uint32_t> items;
+  items.reserve((size_t)(tiles * (D + 1)));
+  for (int64_t t = 0; t < tiles; ++t) {
+    for (int r = 0; r < D; ++r) items.push_back(((uint32_t)r << 24) | (uint32_t)t);
+    if (t >= lag) items.push_back(agmm::kArReduceItem | (uint32_t)(t - lag));
+  }
+  for (int64_t t = std::max<int64_t>(0, tiles - lag); t < tiles; ++t)
+    items.push_back(agmm::kArReduceItem | (uint32_t)t);
+  return items;
+}
+
+// The planner descriptor of one rank's share: a one-shard GEMM over K_local, read in place.
+agmm_desc ar_share_desc(int64_t M, int64_t N, int64_t K_local, int dtype, int block_m) {
+  agmm_desc d;
+  ag_matmul_desc_init(&d);
+  d.M = M;
+  d.N = N;
+  d.K = K_local;
+  d.dtype = dtype;
+  d.algo = AGMM_ALGO_BASELINE;
+  d.block_m = block_m;
+  return d;
+}
+
 // gather: called as ag_matmul_run_gather; a_gathered is then the caller's [M, K] buffer,
 // which serves as the staging buffer (NULL allowed only when it has no bytes).
 int run_impl(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
@@ -789,14 +819,7 @@ int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, in
   if (D < 1 || D > AGMM_MAX_SHARDS || rank < 0 || rank >= D) return AGMM_ERR_INVALID_ARG;
   // one rank's share is a plain GEMM over its K columns: the planner's one-shard,
   // read-in-place case (no fetch units, no staging), run by the atomic-epilogue kernel
-  agmm_desc d;
-  ag_matmul_desc_init(&d);
-  d.M = M;
-  d.N = N;
-  d.K = K_local;
-  d.dtype = dtype;
-  d.algo = AGMM_ALGO_BASELINE;
-  d.block_m = block_m;
+  agmm_desc d = ar_share_desc(M, N, K_local, dtype, block_m);
   const int rc = ag_matmul_create(&d, out_handle);
   if (rc != AGMM_OK) return rc;
   (*out_handle)->ar_D = D;
@@ -872,20 +895,8 @@ int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dt
   int rc = ag_gemm_ar_create(D, 0, M, N, K_local, dtype, block_m, &h);
   if (rc != AGMM_OK) return rc;
   const agmm_config& c = h->cfg;
+  const std::vector<uint32_t> items = ar_flag_items(D, (int64_t)c.T_m * c.T_n, c.num_cus);
   const int64_t tiles = (int64_t)c.T_m * c.T_n;
-  // Item order: tile by tile, its D producers; tile t's reducer follows the producers of
-  // tile t + lag, lag = the tiles whose producers one round of the grid covers, so that a
-  // reducer mostly finds its flags set.
-  const int64_t grid_max = std::max<int64_t>(1, c.num_cus);
-  const int64_t lag = (grid_max + D - 1) / D;
-  std::vector<uint32_t> items;
-  items.reserve((size_t)(tiles * (D + 1)));
-  for (int64_t t = 0; t < tiles; ++t) {
-    for (int r = 0; r < D; ++r) items.push_back(((uint32_t)r << 24) | (uint32_t)t);
-    if (t >= lag) items.push_back(agmm::kArReduceItem | (uint32_t)(t - lag));
-  }
-  for (int64_t t = std::max<int64_t>(0, tiles - lag); t < tiles; ++t)
-    items.push_back(agmm::kArReduceItem | (uint32_t)t);
   h->ar_flags_mode = true;
   h->ar_items_n = (int64_t)items.size();
   h->ar_flags_n = D * tiles;
@@ -1060,6 +1071,25 @@ int ag_matmul_plan_query(const agmm_desc* desc, int num_cus, int what, void* dst
     case AGMM_Q_CHUNK_MTILES: return put(pl.c_mtiles.data(), pl.c_mtiles.size() * 4);
     default: return AGMM_ERR_INVALID_ARG;
   }
+}
+
+int ag_gemm_ar_flags_plan(int D, int64_t M, int64_t N, int64_t K_local, int dtype, int block_m,
+                          int num_cus, agmm_config* cfg, uint32_t* items, int64_t* count) {
+  if (!count || num_cus < 1 || D < 1 || D > AGMM_MAX_SHARDS) return AGMM_ERR_INVALID_ARG;
+  const agmm_desc d = ar_share_desc(M, N, K_local, dtype, block_m);
+  int rc = validate_desc(&d);
+  if (rc != AGMM_OK) return rc;
+  Plan pl;
+  rc = make_plan(d, num_cus, &pl);
+  if (rc != AGMM_OK) return rc;
+  const std::vector<uint32_t> v = ar_flag_items(D, (int64_t)pl.cfg.T_m * pl.cfg.T_n, num_cus);
+  if (cfg) *cfg = pl.cfg;
+  if (items) {
+    if (*count != (int64_t)v.size()) return AGMM_ERR_INVALID_ARG;
+    if (!v.empty()) memcpy(items, v.data(), v.size() * 4);
+  }
+  *count = (int64_t)v.size();
+  return AGMM_OK;
 }
 
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {

@@ -241,6 +241,14 @@ int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dt
 int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void* const* B_parts,
                          const void* bias, void* out, void* hip_stream);
 
+/* Host only (no device is touched): the configuration (into cfg, unless NULL) and the claim
+ * order of the items that ag_gemm_ar_flags_create would build for these arguments on a
+ * device of num_cus compute units. items NULL: *count is set to the number of items.
+ * Otherwise *count must be that number and items receives them: (r << 24) | tile for rank
+ * r's partial tile, (1 << 30) | tile for the tile's reduction, tile = t_m * T_n + t_n. */
+int ag_gemm_ar_flags_plan(int D, int64_t M, int64_t N, int64_t K_local, int dtype, int block_m,
+                          int num_cus, agmm_config* cfg, uint32_t* items, int64_t* count);
+
 /* Synchronizes the handle's device and frees its workspace (and a pipelined handle's
  * streams and events). NULL-safe. */
 int ag_matmul_destroy(agmm_handle* h);
