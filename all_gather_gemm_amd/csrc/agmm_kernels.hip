@@ -724,9 +724,9 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   // atomic issued from it would touch 32 cache lines; instead each wave passes its block
   // through LDS 32 rows at a time and reads it back so that one instruction's lanes cover
   // consecutive columns of one row (two 128-byte lines at WTN >= 64).
-  // EPI 2 (the per-tile flag variant): the same read-back, with plain stores of the fp32
-  // tile into rank src's partial buffer p.partials + src * M * N ([M][N]); the caller
-  // publishes it.
+  // EPI 2 (the per-tile flag variant): the same pass through LDS, read back as 16-byte row
+  // pieces and stored plainly into rank src's partial buffer p.partials + src * M * N
+  // ([M][N]); the caller publishes it.
   if constexpr (EPI == 1 || EPI == 2) {
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
@@ -756,15 +756,29 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
       __syncthreads();
       const int tr0 = wm * T::WTM + fm * 32;  // tile row of the block's first row
       const int tc0 = wn * T::WTN;            // tile column of its first column
+      if constexpr (EPI == 2) {
+        // plain stores: a lane takes 4 consecutive columns of one row (16-byte LDS reads
+        // and global stores; N, and so cols_valid, is a multiple of 8)
+        constexpr int L4 = T::WTN / 4;  // lanes per row
+        constexpr int R4 = 64 / L4;     // rows per instruction
+        const int rl4 = lane / L4, c4 = (lane % L4) * 4;
+        float* dst = p.partials + (int64_t)src * p.M * p.N;
 #pragma unroll
-      for (int v0 = 0; v0 < NV; v0 += VG) {
-        float x[VG];
-#pragma unroll
-        for (int k = 0; k < VG; ++k) {
-          const int v = v0 + k;
-          x[k] = blk[((v / CPL) * RPI + rl) * RS + (v % CPL) * LPR + cl];
+        for (int i = 0; i < 32 / R4; ++i) {
+          const int r = i * R4 + rl4, tr = tr0 + r, tc = tc0 + c4;
+          const f32x4 v = *reinterpret_cast<lds_f32x4*>(blk + r * RS + c4);
+          if (tr < rows_valid && tc < cols_valid)
+            *reinterpret_cast<f32x4*>(dst + (m0 + tr) * p.N + n0 + tc) = v;
         }
-        if constexpr (EPI == 1) {
+      } else {
+#pragma unroll
+        for (int v0 = 0; v0 < NV; v0 += VG) {
+          float x[VG];
+#pragma unroll
+          for (int k = 0; k < VG; ++k) {
+            const int v = v0 + k;
+            x[k] = blk[((v / CPL) * RPI + rl) * RS + (v % CPL) * LPR + cl];
+          }
           for (int i = 0; i < p.ar_D; ++i) {
             float* dst = p.ar_out[(p.ar_rank + 1 + i) % p.ar_D];
 #pragma unroll
@@ -775,14 +789,6 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
                 __hip_atomic_fetch_add(dst + (m0 + tr) * p.N + n0 + tc, x[k], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
-          }
-        } else {
-          float* dst = p.partials + (int64_t)src * p.M * p.N;
-#pragma unroll
-          for (int k = 0; k < VG; ++k) {
-            const int v = v0 + k;
-            const int tr = tr0 + (v / CPL) * RPI + rl, tc = tc0 + (v % CPL) * LPR + cl;
-            if (tr < rows_valid && tc < cols_valid) dst[(m0 + tr) * p.N + n0 + tc] = x[k];
           }
         }
       }
