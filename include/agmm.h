@@ -174,7 +174,11 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
  * the stream work completes. One run may be in flight per handle; successive runs on one
  * stream are safe; concurrent runs of one handle on different streams are undefined.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
- * or (debug) TIMEOUT.
+ * or (debug) TIMEOUT. Without debug, the run does not synchronize, so a flag wait that
+ * exceeds the spin limit is not in the return code: the kernel records it in the handle's
+ * status word (ag_matmul_debug_query with AGMM_Q_STATUS, after the stream work completes),
+ * its workgroups stop early, and every later run of the handle does no work until it is
+ * destroyed and created again. The same holds for the per-tile flag all-reduce's waits.
  */
 int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
                   void* out, void* hip_stream);
