@@ -96,6 +96,14 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run all_gather_gemm_amd/build.py "
                           "(or __graft_entry__.build()) first")
+    # torch first: it brings its own copy of the HIP runtime, and the library must bind to
+    # that same copy (its runtime symbols resolve to whatever libamdhip64 is loaded first).
+    # Loaded the other way round, the process holds two runtimes, and the library's calls
+    # then fail with "no device" while torch's work.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
     lib.ag_matmul_desc_init.argtypes = [ctypes.POINTER(agmm_desc)]

@@ -151,3 +151,17 @@ def test_struct_layout_matches_header(A, tmp_path):
         assert got[(sname, "size")] == ctypes.sizeof(cls), sname
         for f, _ in cls._fields_:
             assert got[(sname, f)] == getattr(cls, f).offset, (sname, f)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """The package binds the library to torch's HIP runtime: imported before torch, it must
+    not load a second libamdhip64 (the library's calls then report no device while torch's
+    work)."""
+    import subprocess
+    import sys
+    code = ("import all_gather_gemm_amd, torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))), timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip() == "1", r.stdout
