@@ -39,7 +39,7 @@ EXPORTED = [
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
-    "ag_gemm_ar_flags_plan",
+    "ag_gemm_ar_flags_plan", "ag_matmul_sync_status",
 ]
 
 
@@ -108,7 +108,9 @@ def _load():
     vp = ctypes.c_void_p
     lib.ag_matmul_desc_init.argtypes = [ctypes.POINTER(agmm_desc)]
     lib.ag_matmul_desc_init.restype = None
-    lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp)]
+    lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), vp, ctypes.c_size_t,
+                                     ctypes.POINTER(vp)]
+    lib.ag_matmul_sync_status.argtypes = [vp]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.ag_matmul_run_gather.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]
     lib.ag_matmul_plan_query.argtypes = [ctypes.POINTER(agmm_desc), ctypes.c_int, ctypes.c_int,
@@ -153,9 +155,11 @@ def ag_matmul_desc_init(**fields) -> agmm_desc:
     return d
 
 
-def ag_matmul_create(desc: agmm_desc) -> int:
+def ag_matmul_create(desc: agmm_desc, workspace: Optional[int] = None,
+                     workspace_bytes: int = 0) -> int:
     h = ctypes.c_void_p()
-    rc = lib.ag_matmul_create(ctypes.byref(desc), ctypes.byref(h))
+    rc = lib.ag_matmul_create(ctypes.byref(desc), ctypes.c_void_p(workspace) if workspace else None,
+                              workspace_bytes, ctypes.byref(h))
     if rc != AGMM_OK:
         raise AgmmError(rc, "ag_matmul_create")
     return h.value
@@ -205,6 +209,10 @@ def ag_matmul_plan_query(desc: agmm_desc, num_cus: int = 256) -> dict:
             m0 += int(b)
         out["chunks"] = chunks
     return out
+
+
+def ag_matmul_sync_status(handle: int) -> int:
+    return lib.ag_matmul_sync_status(ctypes.c_void_p(handle))
 
 
 def ag_matmul_destroy(handle: Optional[int]) -> int:
@@ -374,6 +382,11 @@ class AgMatmul:
 
     def status(self) -> np.ndarray:
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STATUS, 16), dtype="<u4")
+
+    def sync_status(self) -> int:
+        """Waits for the device; AGMM_OK, or the TIMEOUT / POISONED code of a recorded
+        flag-wait timeout."""
+        return ag_matmul_sync_status(self.handle)
 
     def trace(self):
         c = self.config

@@ -25,7 +25,9 @@ struct agmm_handle {
   agmm_desc desc;
   agmm_config cfg;
   int64_t M_s;
-  char* ws;                 // one device allocation, carved below
+  char* ws;                 // one device allocation (or the caller's workspace), carved below
+  bool own_ws;              // ws was allocated by create (freed by destroy)
+  uint32_t* host_status;    // pinned host mirror of the status words {status, wg, flag, seen}
   uint16_t* staging;
   uint32_t* flags;
   uint32_t* ctr;
@@ -418,6 +420,15 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// A flag-wait timeout of an earlier launch, copied to the handle's pinned host word by that
+// launch's last workgroup: poisons the handle. Reads the word without synchronizing, so a
+// launch still running is seen by a later call (or by ag_matmul_sync_status).
+bool timed_out(agmm_handle* h) {
+  if (__atomic_load_n(&h->host_status[0], __ATOMIC_ACQUIRE) == 0) return false;
+  h->poisoned = true;
+  return true;
+}
+
 // Destroys the pipeline's streams and events created so far (errors ignored: teardown).
 void release_streams(agmm_handle* h) {
   for (int j = 0; j < h->n_pstreams; ++j) (void)hipStreamDestroy(h->pstreams[j]);
@@ -468,9 +479,11 @@ int64_t ag_matmul_workspace_bytes(const agmm_desc* desc) {
   return pl.total;
 }
 
-int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
+int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_bytes,
+                     agmm_handle** out_handle) {
   if (!out_handle) return AGMM_ERR_INVALID_ARG;
   *out_handle = nullptr;
+  if (workspace && ((uintptr_t)workspace & 255u) != 0) return AGMM_ERR_INVALID_ARG;
   int rc = validate_desc(desc);
   if (rc != AGMM_OK) return rc;
   int dev = 0;
@@ -501,10 +514,30 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   h->chunks = pl.chunks;
   h->n_pstreams = 0;
   h->n_events = 0;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)pl.total);
+  if (workspace && workspace_bytes < (size_t)pl.total) {
+    delete h;
+    return AGMM_ERR_INVALID_ARG;
+  }
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&h->host_status), 4 * sizeof(uint32_t),
+                               hipHostMallocCoherent);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
     (void)hipGetLastError();
+    delete h;
+    return e == hipErrorOutOfMemory ? AGMM_ERR_OOM : AGMM_ERR_HIP;
+  }
+  memset(h->host_status, 0, 4 * sizeof(uint32_t));
+  h->own_ws = workspace == nullptr;
+  if (h->own_ws) {
+    e = hipMalloc(reinterpret_cast<void**>(&h->ws), (size_t)pl.total);
+  } else {
+    h->ws = static_cast<char*>(workspace);
+    e = hipSuccess;
+  }
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    (void)hipGetLastError();
+    (void)hipHostFree(h->host_status);
     delete h;
     return e == hipErrorOutOfMemory ? AGMM_ERR_OOM : AGMM_ERR_HIP;
   }
@@ -527,7 +560,8 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   auto fail = [&](hipError_t err) {
     g_last_hip = (int)err;
     release_streams(h);
-    (void)hipFree(h->ws);
+    if (h->own_ws) (void)hipFree(h->ws);
+    (void)hipHostFree(h->host_status);
     delete h;
     return AGMM_ERR_HIP;
   };
@@ -535,6 +569,15 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle) {
   // tables are uploaded once.
   if ((e = hipMemset(h->ws + pl.off_flags, 0, (size_t)(pl.off_units - pl.off_flags))) != hipSuccess)
     return fail(e);
+  {
+    // the kernels copy a recorded timeout to the host word through its device address
+    void* dptr = nullptr;
+    if ((e = hipHostGetDevicePointer(&dptr, h->host_status, 0)) != hipSuccess) return fail(e);
+    const uint32_t words[2] = {(uint32_t)(uintptr_t)dptr, (uint32_t)((uint64_t)(uintptr_t)dptr >> 32)};
+    if ((e = hipMemcpy(h->ctr + agmm::CTR_HOST_LO, words, sizeof(words), hipMemcpyHostToDevice)) !=
+        hipSuccess)
+      return fail(e);
+  }
   if (pl.trace_wgs &&
       (e = hipMemset(h->ws + pl.off_trace, 0, (size_t)(pl.total - pl.off_trace))) != hipSuccess)
     return fail(e);
@@ -585,8 +628,9 @@ int ag_matmul_destroy(agmm_handle* h) {
   if (hipGetDevice(&cur) == hipSuccess && cur != h->cfg.device) (void)hipSetDevice(h->cfg.device);
   hipError_t e = hipDeviceSynchronize();
   release_streams(h);
-  if (e == hipSuccess) e = hipFree(h->ws);
+  if (e == hipSuccess && h->own_ws) e = hipFree(h->ws);
   if (e == hipSuccess && h->ar_ws) e = hipFree(h->ar_ws);
+  if (e == hipSuccess) e = hipHostFree(h->host_status);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
     rc = AGMM_ERR_HIP;
@@ -600,6 +644,16 @@ int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg) {
   if (!h || !cfg) return AGMM_ERR_INVALID_ARG;
   *cfg = h->cfg;
   return AGMM_OK;
+}
+
+int ag_matmul_sync_status(agmm_handle* h) {
+  if (!h) return AGMM_ERR_INVALID_ARG;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != h->cfg.device) return AGMM_ERR_WRONG_DEVICE;
+  AGMM_HIP(hipDeviceSynchronize());
+  if (h->poisoned) return AGMM_ERR_POISONED;
+  return timed_out(h) ? AGMM_ERR_TIMEOUT : AGMM_OK;
 }
 
 }  // extern "C"
@@ -648,7 +702,7 @@ KParams run_params(agmm_handle* h, const void* const* shards, const void* B, con
   p.debug = d.debug;
   p.trace_cap = c.trace_cap;
   p.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpinLimit;
-  p.skip_unit = d.debug ? d.debug_skip_unit : -1;
+  p.skip_unit = d.debug_skip_unit;
   return p;
 }
 
@@ -688,6 +742,7 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
              void* out, bool gather, void* a_gathered, void* hip_stream) {
   if (!h || h->ar_D) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
+  if (timed_out(h)) return AGMM_ERR_TIMEOUT;
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
   int cur = 0;
@@ -820,7 +875,7 @@ int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, in
   // one rank's share is a plain GEMM over its K columns: the planner's one-shard,
   // read-in-place case (no fetch units, no staging), run by the atomic-epilogue kernel
   agmm_desc d = ar_share_desc(M, N, K_local, dtype, block_m);
-  const int rc = ag_matmul_create(&d, out_handle);
+  const int rc = ag_matmul_create(&d, nullptr, 0, out_handle);
   if (rc != AGMM_OK) return rc;
   (*out_handle)->ar_D = D;
   (*out_handle)->ar_rank = rank;
@@ -831,6 +886,7 @@ int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, flo
                    void* hip_stream) {
   if (!h || !h->ar_D || h->ar_flags_mode || !C) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
+  if (timed_out(h)) return AGMM_ERR_TIMEOUT;
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
   int cur = 0;
@@ -928,6 +984,7 @@ int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void*
                          const void* bias, void* out, void* hip_stream) {
   if (!h || !h->ar_flags_mode || !A_parts || !B_parts) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
+  if (timed_out(h)) return AGMM_ERR_TIMEOUT;
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
   int cur = 0;

@@ -35,6 +35,8 @@ enum : int {
   CTR_STATUS_WG = 3,    // workgroup that timed out
   CTR_STATUS_FLAG = 4,  // flag index it waited on
   CTR_STATUS_SEEN = 5,  // flag value it last saw
+  CTR_HOST_LO = 6,      // device address of the handle's host-visible status mirror
+  CTR_HOST_HI = 7,      // (uint32[4], pinned host memory), low and high words; 0 = none
   CTR_FETCH = 64,       // next fetch unit to claim (own 128-byte line)
   CTR_Q = 96,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
   CTR_QSTRIDE = 32,
@@ -80,6 +82,11 @@ struct KParams {
     const uint16_t* ar_B[AGMM_MAX_SHARDS];
   };
 };
+// Every kernel of the library takes this struct by value, and its size fixes the kernel
+// argument block (1312 bytes plus the runtime's hidden arguments, 1568 in all). The block
+// is kept at the size every kernel has been run and profiled with; a new per-launch table
+// goes into the workspace instead of growing the struct.
+static_assert(sizeof(KParams) == 1312, "kernel argument block size");
 
 // Launchers (defined in agmm_kernels.hip). block_m selects the tile family.
 hipError_t launch_fused(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);

@@ -271,6 +271,24 @@ __device__ inline bool aborted(const KParams& p) {
   return __hip_atomic_load(p.ctr + CTR_STATUS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
+// Called by the last workgroup of a launch (every other workgroup has counted itself done,
+// so no wait of this launch is still running): a recorded flag-wait timeout is copied into
+// the handle's pinned host word (CTR_HOST_*), which the host reads at the next run without
+// synchronizing. Nothing is written while the status is clear.
+__device__ inline void mirror_status(const KParams& p) {
+  const uint32_t st = __hip_atomic_load(p.ctr + CTR_STATUS, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hp = (uint64_t)p.ctr[CTR_HOST_LO] | ((uint64_t)p.ctr[CTR_HOST_HI] << 32);
+  if (st == 0 || hp == 0) return;
+  uint32_t* h = reinterpret_cast<uint32_t*>(hp);
+  for (int i = 1; i < 4; ++i)
+    __hip_atomic_store(h + i,
+                       __hip_atomic_load(p.ctr + CTR_STATUS + i, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(h, st, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Waits (every lane of the calling wave) until flags[idx] == target. No acquire: the caller
 // issues one for every flag it has seen complete.
 __device__ inline void poll_flag(const KParams& p, int64_t idx, uint32_t target, Tracer& tr) {
@@ -1223,6 +1241,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
                            __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mirror_status(p);
     }
   }
 }
@@ -1315,6 +1334,7 @@ __global__ __launch_bounds__(kThreads) void agmm_ar_flags(KParams p) {
         __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mirror_status(p);
     }
   }
 }

@@ -97,7 +97,8 @@ typedef struct agmm_desc {
   int32_t num_wgs;       /* workgroups in the persistent grid; 0 = one per compute unit */
   int32_t trace_cap;     /* debug trace records per workgroup; 0 = auto */
   uint32_t spin_limit;   /* flag polls before a wait gives up; 0 = auto (several seconds) */
-  int32_t debug_skip_unit; /* debug: fetch unit whose flag is never published; -1 = none */
+  int32_t debug_skip_unit; /* test knob (any mode): fetch unit whose flag is never
+                              published, so the waits on it time out; -1 = none */
   int32_t tail_split;    /* 1: when the tiles leave a last round at most half full, its
                             tiles are split along K into pieces (fp32 partial sums, added
                             in piece order by the piece that finishes last) so every
@@ -151,18 +152,28 @@ void ag_matmul_desc_init(agmm_desc* desc);
 
 /*
  * Creates a handle for one problem shape on the current HIP device: validates `desc`,
- * chooses the tile configuration, and allocates and zeroes the workspace (staging buffer
- * of M*K elements unless gather_a, flags[T_m*G] uint32, schedule tables, counters, optional trace). This is
- * the preamble of the iris issue ("API / config changes": ..._preamble), done once so that
- * run() allocates nothing. AGMM_ALGO_PIPELINED handles also create their HIP streams (up to
- * 3, default priority, non-blocking) and events here.
- * Returns AGMM_OK and *out_handle, or INVALID_ARG / UNSUPPORTED / OOM / HIP.
+ * chooses the tile configuration, and sets up the workspace (staging buffer of M*K elements
+ * unless gather_a, flags[T_m*G] uint32, schedule tables, counters, optional trace), zeroing
+ * the flags and counters and uploading the tables. This is the preamble of the iris issue
+ * ("API / config changes": ..._preamble), done once so that run() allocates nothing.
+ *   workspace: NULL: the library allocates the workspace (hipMalloc) and frees it in
+ *              destroy. Otherwise caller-owned device memory of at least workspace_bytes
+ *              bytes, 256-byte aligned, which must hold ag_matmul_workspace_bytes(desc)
+ *              bytes; the caller keeps it alive and untouched until destroy has returned,
+ *              and frees it afterwards. One workspace serves one handle at a time.
+ * Every handle also owns 16 bytes of pinned host memory (hipHostMalloc) into which its
+ * kernels copy a flag-wait timeout (see ag_matmul_run).
+ * AGMM_ALGO_PIPELINED handles also create their HIP streams (up to 3, default priority,
+ * non-blocking) and events here.
+ * Returns AGMM_OK and *out_handle, or INVALID_ARG (also: a misaligned or too small
+ * workspace) / UNSUPPORTED / OOM / HIP.
  * Shape rules: M % D == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows); m_contiguous also
  * needs M % 8 == 0. M, N, K may be zero (run() then only writes what exists: K == 0 gives
  * out = bias or 0). M < 2^23, N and K < 2^22, and at most 2^24 output tiles (UNSUPPORTED
  * otherwise).
  */
-int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
+int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_bytes,
+                     agmm_handle** out_handle);
 
 /*
  * Enqueues one run on `hip_stream` (a hipStream_t; NULL = the null stream) and returns
@@ -174,11 +185,13 @@ int ag_matmul_create(const agmm_desc* desc, agmm_handle** out_handle);
  * the stream work completes. One run may be in flight per handle; successive runs on one
  * stream are safe; concurrent runs of one handle on different streams are undefined.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
- * or (debug) TIMEOUT. Without debug, the run does not synchronize, so a flag wait that
- * exceeds the spin limit is not in the return code: the kernel records it in the handle's
- * status word (ag_matmul_debug_query with AGMM_Q_STATUS, after the stream work completes),
- * its workgroups stop early, and every later run of the handle does no work until it is
- * destroyed and created again. The same holds for the per-tile flag all-reduce's waits.
+ * or TIMEOUT. A flag wait that exceeds the spin limit makes every workgroup of the launch
+ * stop early (the output is then incomplete); the launch's last workgroup copies the
+ * status words into the handle's pinned host word. In debug mode run() synchronizes and
+ * returns TIMEOUT for that run itself. Otherwise run() does not synchronize: the first
+ * later call on the handle (run, or ag_matmul_sync_status, which waits for the device)
+ * that finds the word set returns TIMEOUT and poisons the handle; calls after that return
+ * POISONED. The same holds for the GEMM + all-reduce entry points.
  */
 int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
                   void* out, void* hip_stream);
@@ -269,6 +282,11 @@ int ag_matmul_last_hip_error(void);
 
 /* Copies the resolved configuration. */
 int ag_matmul_get_config(const agmm_handle* h, agmm_config* cfg);
+
+/* Waits for the handle's device (hipDeviceSynchronize), then reports whether a launch of the
+ * handle recorded a flag-wait timeout: AGMM_OK if none, TIMEOUT the first time one is found
+ * (the handle is then poisoned), POISONED afterwards; or WRONG_DEVICE / HIP. */
+int ag_matmul_sync_status(agmm_handle* h);
 
 /* ---- debug / bookkeeping access (synchronizes the handle's device) ---- */
 #define AGMM_Q_FLAGS 1        /* uint32[T_m * G] ready flags */

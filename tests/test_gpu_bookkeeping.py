@@ -166,6 +166,85 @@ def test_flag_wait_is_bounded():
     op.close()
 
 
+def test_flag_wait_timeout_reported_without_debug():
+    """The same never-published unit with debug off: run() returns at once (AGMM_OK, nothing
+    synchronized), the kernel's bounded wait gives up and every workgroup exits; the launch's
+    last workgroup copies the status to the handle's host word, so ag_matmul_sync_status
+    (or, without it, the next run) reports TIMEOUT and later calls POISONED. A handle
+    without the skipped unit reports nothing."""
+    import torch
+    import all_gather_gemm_amd as A
+    w = Workload("skip_nodebug", 2, 2 * 128, 256, 512, "f16", "uniform", False, "k_contiguous",
+                 True, 52)
+    inp = make_inputs(w).to("cuda")
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    ptrs = [t.data_ptr() for t in inp.shards]
+
+    def run(op):
+        return A.ag_matmul_run(op.handle, ptrs, inp.B.data_ptr(), None, out.data_ptr(), s)
+
+    kw = dict(block_m=64, k_per_flag=1, spin_limit=2000)
+    for algo in ("fused",):
+        op = A.AgMatmul(w.D, w.M, w.N, w.K, algo=algo, debug_skip_unit=1, **kw)
+        assert run(op) == 0
+        assert op.sync_status() == -5          # TIMEOUT
+        st = op.status()
+        assert st[0] == 1
+        u = op.units()[1]
+        assert st[2] == u[0] * op.config.G + u[1]
+        assert run(op) == -7                   # POISONED
+        assert op.sync_status() == -7
+        op.close()
+        # no sync call: the next run finds the host word set
+        op = A.AgMatmul(w.D, w.M, w.N, w.K, algo=algo, debug_skip_unit=1, **kw)
+        assert run(op) == 0
+        torch.cuda.synchronize()
+        assert run(op) == -5
+        assert run(op) == -7
+        op.close()
+    good = A.AgMatmul(w.D, w.M, w.N, w.K, **kw)
+    for _ in range(3):
+        assert run(good) == 0
+    assert good.sync_status() == 0
+    good.close()
+
+
+def test_caller_workspace():
+    """A handle created on caller-owned device memory (ag_matmul_workspace_bytes of it)
+    computes the same output, bit for bit, as one whose workspace the library allocates; a
+    misaligned or too small workspace is refused."""
+    import torch
+    import all_gather_gemm_amd as A
+    w = Workload("ws", 4, 4 * 192, 520, 776, "f16", "normal_sqrtk", True, "m_contiguous", True,
+                 53, rank=2)
+    inp = make_inputs(w).to("cuda")
+    ref = A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True)
+    want = out_bits(ref.run(inp.shards, inp.B, inp.bias))
+    ref.close()
+    desc = A.ag_matmul_desc_init(D=w.D, M=w.M, N=w.N, K=w.K, rank=w.rank, has_bias=1,
+                                 layout=A.M_CONTIGUOUS)
+    nbytes = A.ag_matmul_workspace_bytes(desc)
+    assert nbytes > 0
+    ws = torch.empty(nbytes + 512, dtype=torch.uint8, device="cuda")
+    base = (ws.data_ptr() + 255) // 256 * 256
+    for bad_ptr, bad_n in ((base + 16, nbytes), (base, nbytes - 256)):
+        with pytest.raises(A.AgmmError) as e:
+            A.ag_matmul_create(desc, bad_ptr, bad_n)
+        assert e.value.code == -1
+    h = A.ag_matmul_create(desc, base, nbytes)
+    out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    for _ in range(2):
+        out.fill_(float("nan"))
+        rc = A.ag_matmul_run(h, [t.data_ptr() for t in inp.shards], inp.B.data_ptr(),
+                             inp.bias.data_ptr(), out.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), want)
+    A.ag_matmul_destroy(h)
+
+
 @pytest.mark.parametrize("w", CASES[:3], ids=lambda w: w.name)
 @pytest.mark.parametrize("kpf,nf", [(2, 5), (32, 64)], ids=["kloop_waits", "row_waits"])
 def test_gather_a_bookkeeping(w, kpf, nf):

@@ -241,3 +241,30 @@ def test_planted_mistakes_are_caught():
     assert not np.allclose(oracle.agmm(dt, _split(A2, 2), B)[0], lib, rtol=1e-6)
     # a flipped sign on B
     assert not np.allclose(oracle.agmm(dt, _split(A, 2), B ^ 0x8000)[0], lib, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dt", [oracle.F16, oracle.BF16])
+def test_check_tolerance_edge(dt):
+    """The pass/fail edge of the output check sits exactly at |got - C| = rtol*|C| + atol, with
+    C the unrounded reference: an error of 0.99 of the tolerance passes and 1.01 fails, on
+    both sides of C, where the relative term dominates (|C| large) and where the absolute
+    term does (|C| small). A check built with a wrong rtol or atol moves the edge and fails
+    one of these."""
+    rtol, atol = oracle.TOL[dt]
+    # representable 16-bit values: large ones (rtol*|g| >> atol) and small ones (<< atol)
+    g = np.array([3.0, -5.5, 96.0, 0.0, 1.0 / 1024, -1.0 / 512])
+    gb = oracle.encode_rne(dt, g)
+    g = oracle.decode(dt, gb)  # exact values of the encoded patterns
+    for f, want_bad in ((0.99, 0), (1.01, len(g))):
+        for side in (1.0, -1.0):
+            # C = g + side * d with d = f * (rtol * |C| + atol); |C| = |g| + side * sign(g) * d
+            # for g != 0 (and |C| = d when g == 0), solved for d
+            s = np.where(g == 0, 1.0, side * np.sign(g))
+            d = f * (rtol * np.abs(g) + atol) / (1.0 - s * f * rtol)
+            C = g + side * d
+            # keep the cases where C stays on g's side of zero (the solved |C| holds there)
+            keep = (g == 0) | (np.sign(C) == np.sign(g))
+            assert keep.sum() >= 4
+            r = oracle.check(dt, gb[keep], C[keep])
+            assert r["bad"] == (want_bad and int(keep.sum())), (f, side, r)
+            assert abs(r["max_ratio"] - f) < 1e-9, (f, side, r)
