@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libagmm.so")
 AGMM_MAX_SHARDS = 64
 AGMM_OK = 0
 ERRORS = {-1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "HIP", -4: "OOM", -5: "TIMEOUT",
-          -6: "WRONG_DEVICE", -7: "POISONED"}
+          -6: "WRONG_DEVICE", -7: "POISONED", -8: "TOO_LARGE"}
 F16, BF16 = 0, 1
 K_CONTIGUOUS, M_CONTIGUOUS = 0, 1
 ALGO_FUSED, ALGO_BASELINE, ALGO_PIPELINED = 0, 1, 2
@@ -39,7 +39,7 @@ EXPORTED = [
     "ag_matmul_get_config", "ag_matmul_debug_query", "ag_matmul_debug_fill_staging",
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
-    "ag_gemm_ar_flags_plan", "ag_matmul_sync_status",
+    "ag_gemm_ar_flags_plan", "ag_matmul_sync_status", "ag_matmul_run_static",
 ]
 
 
@@ -111,6 +111,8 @@ def _load():
     lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), vp, ctypes.c_size_t,
                                      ctypes.POINTER(vp)]
     lib.ag_matmul_sync_status.argtypes = [vp]
+    lib.ag_matmul_run_static.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp), vp, vp,
+                                         vp, vp]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.ag_matmul_run_gather.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]
     lib.ag_matmul_plan_query.argtypes = [ctypes.POINTER(agmm_desc), ctypes.c_int, ctypes.c_int,
@@ -209,6 +211,14 @@ def ag_matmul_plan_query(desc: agmm_desc, num_cus: int = 256) -> dict:
             m0 += int(b)
         out["chunks"] = chunks
     return out
+
+
+def ag_matmul_run_static(desc: agmm_desc, shard_ptrs: Sequence[int], B_ptr: int,
+                         bias_ptr: Optional[int], out_ptr: int, stream: int = 0) -> int:
+    arr = (ctypes.c_void_p * max(1, len(shard_ptrs)))(*[ctypes.c_void_p(p) for p in shard_ptrs])
+    return lib.ag_matmul_run_static(ctypes.byref(desc), arr, ctypes.c_void_p(B_ptr),
+                                    ctypes.c_void_p(bias_ptr) if bias_ptr else None,
+                                    ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
 
 
 def ag_matmul_sync_status(handle: int) -> int:

@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libagmm.so")
-SOURCES = ["agmm_kernels.hip", "agmm_api.cpp"]
+SOURCES = ["agmm_kernels.hip", "agmm_static.hip", "agmm_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

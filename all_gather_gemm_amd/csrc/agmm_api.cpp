@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -412,6 +413,42 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   return AGMM_OK;
 }
 
+// The handle's host-side state from a plan (no device work).
+void init_handle(agmm_handle* h, const agmm_desc& desc, const Plan& pl, int dev) {
+  h->desc = desc;
+  h->cfg = pl.cfg;
+  h->cfg.device = dev;
+  h->M_s = pl.M_s;
+  h->flags_n = pl.flags_n;
+  h->trace_wgs = pl.trace_wgs;
+  h->h_units = pl.units;
+  h->h_mtiles = pl.mtiles;
+  h->h_qtiles = pl.qtiles;
+  memcpy(h->qoff, pl.qoff, sizeof(h->qoff));
+  memcpy(h->qlen, pl.qlen, sizeof(h->qlen));
+  h->poisoned = false;
+  h->chunks = pl.chunks;
+}
+
+// Points the handle's buffers into its workspace h->ws, at the plan's offsets.
+void carve_workspace(agmm_handle* h, const Plan& pl) {
+  h->staging = reinterpret_cast<uint16_t*>(h->ws + pl.off_staging);
+  h->flags = reinterpret_cast<uint32_t*>(h->ws + pl.off_flags);
+  h->ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_ctr);
+  h->units = reinterpret_cast<uint32_t*>(h->ws + pl.off_units);
+  h->mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_mtiles);
+  h->qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_qtiles);
+  h->split_cnt = reinterpret_cast<uint32_t*>(h->ws + pl.off_split);
+  h->partials = reinterpret_cast<float*>(h->ws + pl.off_partials);
+  h->split_base = pl.split_base;
+  h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
+  h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
+  h->c_ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_ctr);
+  h->c_units = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_units);
+  h->c_mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_mtiles);
+  h->c_qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_qtiles);
+}
+
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -424,7 +461,7 @@ bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 // launch's last workgroup: poisons the handle. Reads the word without synchronizing, so a
 // launch still running is seen by a later call (or by ag_matmul_sync_status).
 bool timed_out(agmm_handle* h) {
-  if (__atomic_load_n(&h->host_status[0], __ATOMIC_ACQUIRE) == 0) return false;
+  if (!h->host_status || __atomic_load_n(&h->host_status[0], __ATOMIC_ACQUIRE) == 0) return false;
   h->poisoned = true;
   return true;
 }
@@ -463,6 +500,7 @@ const char* ag_matmul_strerror(int code) {
     case AGMM_ERR_TIMEOUT: return "flag wait timed out";
     case AGMM_ERR_WRONG_DEVICE: return "current device differs from the handle's device";
     case AGMM_ERR_POISONED: return "handle poisoned by an earlier timeout";
+    case AGMM_ERR_TOO_LARGE: return "workspace larger than the static scratch";
     default: return "unknown error code";
   }
 }
@@ -499,19 +537,7 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
 
   agmm_handle* h = new (std::nothrow) agmm_handle();
   if (!h) return AGMM_ERR_OOM;
-  h->desc = *desc;
-  h->cfg = pl.cfg;
-  h->cfg.device = dev;
-  h->M_s = pl.M_s;
-  h->flags_n = pl.flags_n;
-  h->trace_wgs = pl.trace_wgs;
-  h->h_units = pl.units;
-  h->h_mtiles = pl.mtiles;
-  h->h_qtiles = pl.qtiles;
-  memcpy(h->qoff, pl.qoff, sizeof(h->qoff));
-  memcpy(h->qlen, pl.qlen, sizeof(h->qlen));
-  h->poisoned = false;
-  h->chunks = pl.chunks;
+  init_handle(h, *desc, pl, dev);
   h->n_pstreams = 0;
   h->n_events = 0;
   if (workspace && workspace_bytes < (size_t)pl.total) {
@@ -541,21 +567,7 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
     delete h;
     return e == hipErrorOutOfMemory ? AGMM_ERR_OOM : AGMM_ERR_HIP;
   }
-  h->staging = reinterpret_cast<uint16_t*>(h->ws + pl.off_staging);
-  h->flags = reinterpret_cast<uint32_t*>(h->ws + pl.off_flags);
-  h->ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_ctr);
-  h->units = reinterpret_cast<uint32_t*>(h->ws + pl.off_units);
-  h->mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_mtiles);
-  h->qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_qtiles);
-  h->split_cnt = reinterpret_cast<uint32_t*>(h->ws + pl.off_split);
-  h->partials = reinterpret_cast<float*>(h->ws + pl.off_partials);
-  h->split_base = pl.split_base;
-  h->trace = pl.trace_wgs ? reinterpret_cast<agmm_trace_rec*>(h->ws + pl.off_trace) : nullptr;
-  h->trace_count = reinterpret_cast<uint32_t*>(h->ws + pl.off_tcount);
-  h->c_ctr = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_ctr);
-  h->c_units = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_units);
-  h->c_mtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_mtiles);
-  h->c_qtiles = reinterpret_cast<uint32_t*>(h->ws + pl.off_c_qtiles);
+  carve_workspace(h, pl);
 
   auto fail = [&](hipError_t err) {
     g_last_hip = (int)err;
@@ -1147,6 +1159,72 @@ int ag_gemm_ar_flags_plan(int D, int64_t M, int64_t N, int64_t K_local, int dtyp
   }
   *count = (int64_t)v.size();
   return AGMM_OK;
+}
+
+namespace {
+
+// The tables that the current device's scratch holds, by the (descriptor, CU count) they
+// were planned for, so that repeated calls with one shape upload them once.
+struct StaticTables {
+  bool valid;
+  agmm_desc desc;
+  int num_cus;
+};
+std::mutex g_static_mu;
+StaticTables g_static_tables[64];
+
+bool same_desc(const agmm_desc& a, const agmm_desc& b) { return memcmp(&a, &b, sizeof(a)) == 0; }
+
+}  // namespace
+
+int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const void* B,
+                         const void* bias, void* out, void* hip_stream) {
+  int rc = validate_desc(desc);
+  if (rc != AGMM_OK) return rc;
+  if (desc->algo == AGMM_ALGO_PIPELINED || desc->gather_a || desc->debug || desc->tail_split)
+    return AGMM_ERR_UNSUPPORTED;
+  int dev = 0;
+  AGMM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return AGMM_ERR_WRONG_DEVICE;
+  int num_cus = 0;
+  AGMM_HIP(hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+  Plan pl;
+  rc = make_plan(*desc, num_cus, &pl);
+  if (rc != AGMM_OK) return rc;
+  if (pl.total > (int64_t)agmm::kScratchBytes) return AGMM_ERR_TOO_LARGE;
+  int per_cu = 0;
+  AGMM_HIP(agmm::fused_occupancy(desc->dtype, pl.cfg.block_m, &per_cu));
+  if (per_cu < 1) return AGMM_ERR_UNSUPPORTED;
+  void* base = nullptr;
+  AGMM_HIP(agmm::scratch_region(dev, &base));
+
+  // A handle on the host stack, its workspace the scratch; it allocates nothing (the
+  // vectors are host memory) and it has no host status word.
+  agmm_handle h{};
+  init_handle(&h, *desc, pl, dev);
+  h.ws = static_cast<char*>(base);
+  h.own_ws = false;
+  h.host_status = nullptr;
+  carve_workspace(&h, pl);
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  // Flags, counters and split counters start at zero: one fill kernel (not a memset, which
+  // a captured graph would record as a memset node). The run is then epoch 1.
+  AGMM_HIP(agmm::launch_fill32(reinterpret_cast<uint32_t*>(h.ws + pl.off_flags),
+                               (pl.off_units - pl.off_flags) / 4, 0u, s));
+  {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticTables& t = g_static_tables[dev];
+    if (!(t.valid && t.num_cus == num_cus && same_desc(t.desc, *desc))) {
+      t.valid = false;
+      AGMM_HIP(agmm::launch_upload32(h.units, pl.units.data(), (int64_t)pl.units.size(), s));
+      AGMM_HIP(agmm::launch_upload32(h.mtiles, pl.mtiles.data(), (int64_t)pl.mtiles.size(), s));
+      AGMM_HIP(agmm::launch_upload32(h.qtiles, pl.qtiles.data(), (int64_t)pl.qtiles.size(), s));
+      t.valid = true;
+      t.desc = *desc;
+      t.num_cus = num_cus;
+    }
+  }
+  return run_impl(&h, shards, B, bias, out, false, nullptr, hip_stream);
 }
 
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {

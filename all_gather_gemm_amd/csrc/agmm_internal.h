@@ -104,5 +104,15 @@ hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
 hipError_t launch_fill32(uint32_t* dst, int64_t n, uint32_t v, hipStream_t s);
 // Resident workgroups per CU for the fused kernel of this family (occupancy query).
 hipError_t fused_occupancy(int dtype, int block_m, int* per_cu);
+// dst[0 .. n) = src[0 .. n) (host words) by kernels that take the words as arguments, so
+// nothing on the host has to outlive the call and no copy engine or allocation is used.
+hipError_t launch_upload32(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s);
+
+// Size of the per-device scratch array of ag_matmul_run_static (agmm_static.hip): enough
+// for a 64 MiB staging buffer (e.g. 4096 x 8192 16-bit elements) and its tables.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+// The scratch array's device address on `device`, which must be the current device; the
+// address is looked up once per device (hipGetSymbolAddress) and then kept.
+hipError_t scratch_region(int device, void** ptr);
 
 }  // namespace agmm

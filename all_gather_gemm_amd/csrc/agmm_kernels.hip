@@ -1347,6 +1347,19 @@ __global__ __launch_bounds__(kThreads) void agmm_copy(KParams p) {
   copy_units<Tile<BM>>(p, s_shards, blockIdx.x, gridDim.x, threadIdx.x);
 }
 
+// Up to kUploadWords words per launch, carried in the kernel argument (kept well under the
+// size of the other kernels' argument block).
+constexpr int kUploadWords = 256;
+struct UploadWords {
+  uint32_t n;
+  uint32_t w[kUploadWords];
+};
+
+__global__ __launch_bounds__(kUploadWords) void upload32_kernel(uint32_t* dst, UploadWords p) {
+  const uint32_t i = threadIdx.x;
+  if (i < p.n) dst[i] = p.w[i];
+}
+
 __global__ void fill16_kernel(uint16_t* dst, int64_t n, uint16_t v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -1505,6 +1518,18 @@ hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_upload32(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s) {
+  for (int64_t o = 0; o < n; o += kUploadWords) {
+    UploadWords p;
+    p.n = (uint32_t)(n - o < kUploadWords ? n - o : kUploadWords);
+    for (uint32_t i = 0; i < kUploadWords; ++i) p.w[i] = i < p.n ? src[o + i] : 0u;
+    hipLaunchKernelGGL(upload32_kernel, dim3(1), dim3(kUploadWords), 0, s, dst + o, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s) {

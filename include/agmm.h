@@ -47,6 +47,7 @@ extern "C" {
 #define AGMM_ERR_TIMEOUT (-5)      /* a flag wait exceeded its spin limit; handle is poisoned */
 #define AGMM_ERR_WRONG_DEVICE (-6) /* current HIP device differs from the handle's device */
 #define AGMM_ERR_POISONED (-7)     /* an earlier run timed out; destroy and recreate */
+#define AGMM_ERR_TOO_LARGE (-8)    /* ag_matmul_run_static: workspace exceeds the scratch */
 
 /* ---- enumerations ---- */
 #define AGMM_F16 0
@@ -208,6 +209,31 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
  */
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): create + run + destroy of a handle for
+ * `desc` in one call that allocates nothing. Its workspace is a fixed per-device scratch
+ * array of the library (80 MiB, held by each device the library has run this on until the
+ * process ends; its address is looked up once per device); the caller still passes inputs
+ * and outputs exactly as for ag_matmul_run, on the current device.
+ *   desc: as for ag_matmul_create; algo FUSED or BASELINE; debug, gather_a and tail_split
+ *         must be 0 (UNSUPPORTED otherwise). The workspace create would use for it,
+ *         ag_matmul_workspace_bytes(desc) on this device, must fit the scratch, else
+ *         TOO_LARGE and nothing is enqueued: a staging buffer of up to 64 MiB, e.g.
+ *         4096 x 8192 16-bit elements of A.
+ * Enqueues on `hip_stream`: a fill kernel that clears the scratch's flags and counters,
+ * kernels that write the schedule tables (skipped when this device's previous call had the
+ * same desc), then the run's kernels. Nothing is synchronized, and no host memory has to
+ * outlive the call. Every call on one device shares that device's scratch: calls whose
+ * stream work overlaps (other streams, other host threads) race on it and their outputs
+ * are undefined; calls on one stream are ordered and safe. A flag-wait timeout (a fetch
+ * unit never published, which normal runs do not produce) ends the launch early with an
+ * incomplete output and is not reported by this entry point.
+ * Returns AGMM_OK, INVALID_ARG, UNSUPPORTED, TOO_LARGE, WRONG_DEVICE or HIP.
+ */
+int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const void* B,
+                         const void* bias, void* out, void* hip_stream);
 
 /* ---- GEMM + all-reduce, atomics variant: one rank's share ----
  * The mirror op of the all-gather (ROCm/iris PR "Let's make Iris' All-reduce the best!": a
