@@ -40,7 +40,9 @@ EXPORTED = [
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
     "ag_gemm_ar_flags_plan", "ag_matmul_sync_status", "ag_matmul_run_static",
+    "ag_matmul_debug_run_part",
 ]
+PART_COPY, PART_GEMM = 1, 2
 
 
 class agmm_desc(ctypes.Structure):
@@ -111,6 +113,7 @@ def _load():
     lib.ag_matmul_create.argtypes = [ctypes.POINTER(agmm_desc), vp, ctypes.c_size_t,
                                      ctypes.POINTER(vp)]
     lib.ag_matmul_sync_status.argtypes = [vp]
+    lib.ag_matmul_debug_run_part.argtypes = [vp, ctypes.c_int, ctypes.POINTER(vp), vp, vp, vp, vp]
     lib.ag_matmul_run_static.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp), vp, vp,
                                          vp, vp]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
@@ -219,6 +222,14 @@ def ag_matmul_run_static(desc: agmm_desc, shard_ptrs: Sequence[int], B_ptr: int,
     return lib.ag_matmul_run_static(ctypes.byref(desc), arr, ctypes.c_void_p(B_ptr),
                                     ctypes.c_void_p(bias_ptr) if bias_ptr else None,
                                     ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
+
+
+def ag_matmul_debug_run_part(handle: int, part: int, shard_ptrs: Sequence[int], B_ptr: int,
+                             bias_ptr: Optional[int], out_ptr: int, stream: int = 0) -> int:
+    arr = (ctypes.c_void_p * max(1, len(shard_ptrs)))(*[ctypes.c_void_p(p) for p in shard_ptrs])
+    return lib.ag_matmul_debug_run_part(ctypes.c_void_p(handle), part, arr, ctypes.c_void_p(B_ptr),
+                                        ctypes.c_void_p(bias_ptr) if bias_ptr else None,
+                                        ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
 
 
 def ag_matmul_sync_status(handle: int) -> int:
@@ -392,6 +403,20 @@ class AgMatmul:
 
     def status(self) -> np.ndarray:
         return np.frombuffer(ag_matmul_debug_query(self.handle, Q_STATUS, 16), dtype="<u4")
+
+    def run_part(self, part: int, shards, B, bias=None, out=None, check: bool = True):
+        """A baseline handle's copy (PART_COPY) or GEMM (PART_GEMM) phase alone."""
+        import torch
+        d = self.desc
+        tdt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        if out is None:
+            out = torch.empty((d.M, d.N), dtype=tdt, device=B.device)
+        rc = ag_matmul_debug_run_part(self.handle, part, [t.data_ptr() for t in shards],
+                                      B.data_ptr(), bias.data_ptr() if bias is not None else None,
+                                      out.data_ptr(), torch.cuda.current_stream(B.device).cuda_stream)
+        if check and rc != AGMM_OK:
+            raise AgmmError(rc, "ag_matmul_debug_run_part")
+        return out
 
     def sync_status(self) -> int:
         """Waits for the device; AGMM_OK, or the TIMEOUT / POISONED code of a recorded

@@ -750,8 +750,10 @@ agmm_desc ar_share_desc(int64_t M, int64_t N, int64_t K_local, int dtype, int bl
 
 // gather: called as ag_matmul_run_gather; a_gathered is then the caller's [M, K] buffer,
 // which serves as the staging buffer (NULL allowed only when it has no bytes).
+// part (AGMM_ALGO_BASELINE only): 0 = the whole run, AGMM_PART_COPY = only its staging copy,
+// AGMM_PART_GEMM = only its GEMM.
 int run_impl(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
-             void* out, bool gather, void* a_gathered, void* hip_stream) {
+             void* out, bool gather, void* a_gathered, void* hip_stream, int part = 0) {
   if (!h || h->ar_D) return AGMM_ERR_INVALID_ARG;
   if (h->poisoned) return AGMM_ERR_POISONED;
   if (timed_out(h)) return AGMM_ERR_TIMEOUT;
@@ -847,10 +849,12 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
     p.staged_kmajor = 1;  // the baseline gathers into plain [M][K] rows
     p.debug = 0;
     p.trace_cap = 0;
-    if (c.num_units > 0) AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
+    if (c.num_units > 0 && part != AGMM_PART_GEMM)
+      AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
     const int grid = (int)std::min<int64_t>(std::min(c.num_cus, c.num_items),
                                             d.num_wgs ? d.num_wgs : c.num_cus);
-    if (grid > 0) AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
+    if (grid > 0 && part != AGMM_PART_COPY)
+      AGMM_HIP(agmm::launch_gemm_only(p, d.dtype, c.block_m, grid, s));
   }
 
   if (d.debug) {
@@ -877,6 +881,13 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream) {
   return run_impl(h, shards, B, bias, out, true, a_gathered, hip_stream);
+}
+
+int ag_matmul_debug_run_part(agmm_handle* h, int part, const void* const* shards, const void* B,
+                             const void* bias, void* out, void* hip_stream) {
+  if (!h || h->desc.algo != AGMM_ALGO_BASELINE || h->desc.gather_a) return AGMM_ERR_INVALID_ARG;
+  if (part != AGMM_PART_COPY && part != AGMM_PART_GEMM) return AGMM_ERR_INVALID_ARG;
+  return run_impl(h, shards, B, bias, out, false, nullptr, hip_stream, part);
 }
 
 int ag_gemm_ar_create(int D, int rank, int64_t M, int64_t N, int64_t K_local, int dtype,

@@ -10,10 +10,16 @@ time that kernel). TFLOP/s counts 2*M*N*K per step with M the full gathered row 
 convention of the iris issue's results tables.
 
 Prints ONE JSON line on stdout. Unless --no-extras, the line also carries the other
-variants on the same inputs: the copy-barrier-GEMM baseline, the host stream pipeline
-(2, 4, 8 chunks), the variant that also returns the gathered A, and torch.matmul on a
-pre-gathered A as a yardstick. `--sweep` additionally writes a table of all five workloads
-(fused, baseline, pipelined, yardstick) to stderr and, with --out, to a JSON-lines file.
+variants on the same inputs: the copy-barrier-GEMM baseline (runs interleaved with the fused
+ones, and "standalone": each timed back to back in alternating blocks, plus a cold-cache
+series after 1 GiB of unrelated writes), the baseline's copy and GEMM phases timed alone
+(the copy's staging rate against the HBM peak), the shader clock sampled under sustained
+fused load, the host stream pipeline (2, 4, 8 chunks), the variant that also returns the
+gathered A, the GEMM + all-reduce variants, and torch.matmul on a pre-gathered A as a
+yardstick. kernel_resources gives the fused and GEMM kernels' registers, spills and LDS from
+the built code object. `--sweep` additionally writes a table of all five workloads to stderr
+and, with --out, to a JSON-lines file; `--timeline` prints the fused kernel's fetch/GEMM
+overlap from a debug trace instead.
 """
 import argparse
 import json
@@ -214,24 +220,44 @@ def yardstick_matmul(w, dev, steps, warmup, torch):
     return a.elapsed_time(b) / steps
 
 
-KERNEL_SOURCES = ["all_gather_gemm_amd/csrc/agmm_kernels.hip",
-                  "all_gather_gemm_amd/csrc/agmm_internal.h"]
 TRAFFIC_FILE = "profiles/agmm_persistent_fused_16384x3584x8192_f16_hbm_traffic.md"
+RESOURCES_FILE = "all_gather_gemm_amd/kernel_resources.json"
+
+
+def kernel_resources():
+    """The built library's per-kernel registers, spills and LDS (written by the build from the
+    gfx950 code object's metadata), or None when the build did not write them."""
+    try:
+        with open(os.path.join(ROOT, RESOURCES_FILE)) as fh:
+            return json.load(fh)
+    except (OSError, ValueError):
+        return None
+
+
+def kernel_entry(res, block_m, dtype, fused, layout_k, row_wait):
+    """Resources of one agmm_persistent instance (by its mangled template arguments)."""
+    if not res:
+        return None
+    dt = 1 if dtype == "bf16" else 0
+    tag = "agmm_persistentILi%dELi%dELb%dELb%dELb%dELi0EE" % (block_m, dt, int(fused),
+                                                             int(layout_k), int(row_wait))
+    for k, v in res["kernels"].items():
+        if tag in k:
+            return dict(v, symbol=k)
+    return None
 
 
 def measured_traffic(workload_name, algo):
     """HBM bytes per launch of the fused kernel from the committed counter summary (rocprofv3
-    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when that summary does not describe
-    the kernel as it is built now (its recorded source hash differs) or another workload."""
-    import hashlib
+    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when that summary was taken on another
+    build (the code object hash it records differs from the built one) or another workload."""
     if workload_name != "ag_16384x3584x8192_d8_f16_bias" or algo != "fused":
         return None
+    res = kernel_resources()
+    if not res:
+        return None
+    kv = {}
     try:
-        h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
-            with open(os.path.join(ROOT, f), "rb") as fh:
-                h.update(fh.read())
-        kv = {}
         with open(os.path.join(ROOT, TRAFFIC_FILE)) as fh:
             for line in fh:
                 if ":" in line and not line.startswith(("|", "#", "-")):
@@ -239,9 +265,170 @@ def measured_traffic(workload_name, algo):
                     kv[k.strip()] = v.strip()
     except OSError:
         return None
-    if kv.get("kernel_source_sha256") != h.hexdigest():
+    if kv.get("code_object_sha256") != res["code_object_sha256"]:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def sample_sclk(n=4, gap_s=0.3):
+    """Shader clock (MHz) read with rocm-smi n times, gap_s apart (None where unreadable)."""
+    import re
+    import subprocess
+    out = []
+    for i in range(n):
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                               text=True, timeout=20)
+            m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', r.stdout)
+            out.append(int(m.group(1)) if m else None)
+        except Exception:
+            out.append(None)
+        time.sleep(gap_s)
+    return out
+
+
+def clock_under_load(op, dev, torch, seconds=2.0):
+    """Median shader clock while the op runs back to back for about `seconds`."""
+    import threading
+    samples = []
+    th = threading.Thread(target=lambda: samples.extend(sample_sclk(4, seconds / 6)))
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+        torch.cuda.synchronize()
+    th.join()
+    vals = sorted(v for v in samples if v)
+    return {"sclk_mhz_samples": samples, "sclk_mhz_median": vals[len(vals) // 2] if vals else None}
+
+
+def block_times(w, ops, dev, torch, blocks, per):
+    """Median ms per run of each op, each timed back to back in blocks of `per` runs, the
+    blocks of the ops alternating (order reversed every other round): every op runs in its
+    own sustained state, and drift falls on all of them alike."""
+    res = {n: [] for n, _ in ops}
+    for blk in range(blocks):
+        for n, op in (ops if blk % 2 == 0 else ops[::-1]):
+            for _ in range(2):
+                op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(per):
+                op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+            e1.record()
+            torch.cuda.synchronize()
+            res[n].append(e0.elapsed_time(e1) / per)
+    return {n: statistics.median(v) for n, v in res.items()}
+
+
+def cold_times(op, dev, torch, reps, flush_bytes=1 << 30):
+    """ms of single runs, each after 1 GiB of unrelated writes (untimed) have pushed the
+    op's working set out of the caches."""
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    per = []
+    for _ in range(reps):
+        junk.fill_(7)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del junk
+    torch.cuda.empty_cache()
+    return statistics.median(per)
+
+
+def baseline_parts(w, dev, torch, A, reps=20):
+    """The barrier baseline's two phases timed alone (debug entry point): the staging copy
+    (its HBM rate against the peak) and the GEMM over the staged A."""
+    import all_gather_gemm_amd as AA
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo="baseline",
+                    rank=w.rank, direct_local=w.direct_local, has_bias=w.has_bias)
+    out = {}
+    for name, part in (("copy", AA.PART_COPY), ("gemm", AA.PART_GEMM)):
+        for _ in range(3):
+            op.run_part(part, dev.shards, dev.B, dev.bias, out=dev.out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            op.run_part(part, dev.shards, dev.B, dev.bias, out=dev.out)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_ms"] = e0.elapsed_time(e1) / reps
+    op.close()
+    staged = 2 * (w.M - (w.M_s if w.direct_local else 0)) * w.K * 2
+    return {"copy_ms": round(out["copy_ms"], 5), "staging_bytes": staged,
+            "copy_gbs": round(staged / (out["copy_ms"] * 1e-3) / 1e9, 1),
+            "copy_frac_of_hbm_peak": round(staged / (out["copy_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_ms": round(out["gemm_ms"], 5),
+            "gemm_tflops": round(tflops(w.M, w.N, w.K, out["gemm_ms"] * 1e-3), 1)}
+
+
+def timeline(w, torch, A, runs=3, **tun):
+    """Fetch-vs-GEMM overlap of the fused kernel from its debug trace (per-workgroup fetch,
+    tile and wait records, 100 MHz timestamps) on the last of `runs` runs. Debug runs record
+    every event, so absolute times run somewhat longer than timed runs."""
+    from workloads import make_inputs
+    inp = make_inputs(w)
+    dev = inp.to("cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
+                    direct_local=w.direct_local, has_bias=w.has_bias, debug=True, trace_cap=64,
+                    **tun)
+    for _ in range(runs):
+        op.run(dev.shards, dev.B, dev.bias)
+        torch.cuda.synchronize()
+    counts, recs = op.trace()
+    cfg = op.config.as_dict()
+    direct = {int(e & 0x7FFFFFFF) for e in op.mtiles() if e >> 31}
+    ev = []
+    for wg in range(len(counts)):
+        for r in recs[wg, :min(int(counts[wg]), recs.shape[1])]:
+            ev.append((wg, int(r["event"]), int(r["a"]), int(r["t0"]), int(r["t1"])))
+    op.close()
+    t0 = min(e[3] for e in ev)
+    us = lambda t: (t - t0) * 1e-2
+    fetch = [e for e in ev if e[1] == 1]
+    gemm = [e for e in ev if e[1] == 2]
+    wait = [e for e in ev if e[1] == 3]
+    span = us(max(e[4] for e in ev))
+    res = {"workload": w.name, "block_m": cfg["block_m"], "fetch_wgs": cfg["num_fetch_wgs"],
+           "wgs": cfg["num_wgs"], "k_per_flag": cfg["k_per_flag"], "row_wait": cfg["row_wait"],
+           "span_us": round(span, 1)}
+    q = lambda v, f: sorted(v)[int(f * (len(v) - 1))]
+    if fetch:
+        fe = [us(e[4]) for e in fetch]
+        res.update({"units": len(fetch), "fetch_end_us": round(max(fe), 1),
+                    "fetch_end_frac": round(max(fe) / span, 3),
+                    "unit_us_median": round(statistics.median((e[4] - e[3]) * 1e-2 for e in fetch), 2)})
+        # MFMA work that ran while the fetch was still going: tile time inside [0, fetch end]
+        fend = max(e[4] for e in fetch)
+        overl = sum(max(0, min(e[4], fend) - e[3]) for e in gemm) * 1e-2
+        res["tile_us_during_fetch"] = round(overl, 1)
+        res["tile_us_total"] = round(sum((e[4] - e[3]) * 1e-2 for e in gemm), 1)
+    st = [(e[4] - e[3]) * 1e-2 for e in gemm if e[2] not in direct]
+    dr = [(e[4] - e[3]) * 1e-2 for e in gemm if e[2] in direct]
+    if st:
+        res["staged_tile_us_median"] = round(statistics.median(st), 1)
+    if dr:
+        res["direct_tile_us_median"] = round(statistics.median(dr), 1)
+    starts = [us(min(e[3] for e in gemm if e[0] == wg)) for wg in {e[0] for e in gemm}]
+    ends = [us(max(e[4] for e in gemm if e[0] == wg)) for wg in {e[0] for e in gemm}]
+    res["wg_first_tile_start_us_p50_p90_max"] = [round(q(starts, f), 1) for f in (0.5, 0.9, 1.0)]
+    res["wg_last_tile_end_us_min_p50_max"] = [round(q(ends, f), 1) for f in (0.0, 0.5, 1.0)]
+    per = {}
+    for e in gemm:
+        per[e[0]] = per.get(e[0], 0) + 1
+    hist = {}
+    for n in per.values():
+        hist[n] = hist.get(n, 0) + 1
+    res["tiles_per_wg"] = {str(k): v for k, v in sorted(hist.items())}
+    if wait:
+        res["waits"] = len(wait)
+        res["wait_us_total"] = round(sum((e[4] - e[3]) * 1e-2 for e in wait), 1)
+    return res
 
 
 def cpu_baseline(w, inp, gpu_out, target_s):
@@ -289,6 +476,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--fetch-wgs", type=int, default=0)
     ap.add_argument("--k-per-flag", type=int, default=0)
+    ap.add_argument("--timeline", action="store_true",
+                    help="only print the fused kernel's fetch/GEMM timeline from a debug trace "
+                         "(for each of --workload, or of all five workloads with --sweep)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the "
                          "known-size reference for the HBM byte counters")
@@ -318,6 +508,10 @@ def main():
         print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
                           "dispatches": 3}), flush=True)
         return
+    if args.timeline:
+        for w in (WORKLOADS if args.sweep else [BY_NAME[args.workload]]):
+            print(json.dumps(timeline(w, torch, A)), flush=True)
+        return
     tun = {}
     if args.block_m:
         tun["block_m"] = args.block_m
@@ -333,10 +527,18 @@ def main():
                                             args.warmup, torch, A, **tun)
             ym = yardstick_matmul(w, dev, args.steps, args.warmup, torch)
             mf, mb, mp = med["fused"], med["baseline"], med["pipelined"]
+            bops = [(a, A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=a,
+                                   rank=w.rank, direct_local=w.direct_local,
+                                   has_bias=w.has_bias, **tun)) for a in ("fused", "baseline")]
+            bt = block_times(w, bops, dev, torch, 6, 10)
+            for _, op in bops:
+                op.close()
             row = {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "D": w.D,
                    "dtype": w.dtype, "layout": w.layout,
                    "fused_ms_median": mf,
                    "baseline_ms_median": mb, "speedup": mb / mf,
+                   "fused_ms_standalone": bt["fused"], "baseline_ms_standalone": bt["baseline"],
+                   "speedup_standalone": bt["baseline"] / bt["fused"],
                    "pipelined_ms_median": mp,
                    "pipelined_chunks": cfgs["pipelined"]["pipeline_chunks"],
                    "fused_tflops": tflops(w.M, w.N, w.K, mf / 1e3),
@@ -347,7 +549,8 @@ def main():
             rows.append(row)
             print("| {workload} | {fused_ms_median:.4f} | {baseline_ms_median:.4f} | "
                   "{pipelined_ms_median:.4f} (S={pipelined_chunks}) | "
-                  "{speedup:.2f}x | {fused_tflops:.1f} | {pct_peak:.1f}% | "
+                  "{speedup:.2f}x | {fused_ms_standalone:.4f} | {baseline_ms_standalone:.4f} | "
+                  "{speedup_standalone:.3f}x | {fused_tflops:.1f} | {pct_peak:.1f}% | "
                   "{torch_matmul_pregathered_ms:.4f} | {block_m} |".format(**row),
                   file=sys.stderr, flush=True)
             del dev
@@ -389,6 +592,13 @@ def main():
                      "per_launch_flops": 2.0 * w.M * w.N * w.K,
                      "avg_launch_ms": round(avg_ms, 5)},
     }
+    kr = kernel_resources()
+    cfg = r["config"]
+    lk = w.layout == "k_contiguous"
+    res["kernel_resources"] = {
+        "code_object_sha256": kr["code_object_sha256"] if kr else None,
+        "fused": kernel_entry(kr, cfg["block_m"], w.dtype, True, lk, cfg["row_wait"]),
+        "baseline_gemm": kernel_entry(kr, cfg["block_m"], w.dtype, False, True, False)}
     if not args.no_cpu_baseline:   # before the extras reuse the output buffer
         res["cpu_baseline"] = cpu_baseline(w, r["inputs"], r["dev"].out, args.cpu_seconds)
     if not args.no_extras:
@@ -405,6 +615,20 @@ def main():
                                    "fused_speedup": round((mb / med[args.algo])
                                                           if other == "baseline" else
                                                           (med[args.algo] / mb), 3)}
+        if args.algo == "fused":
+            bops = [(a, A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=a,
+                                   rank=w.rank, direct_local=w.direct_local,
+                                   has_bias=w.has_bias, **tun)) for a in ("fused", "baseline")]
+            bt = block_times(w, bops, r["dev"], torch, 6, 10)
+            res["standalone"] = {"fused_ms": round(bt["fused"], 5),
+                                 "baseline_ms": round(bt["baseline"], 5),
+                                 "fused_speedup": round(bt["baseline"] / bt["fused"], 3),
+                                 "cold_fused_ms": round(cold_times(bops[0][1], r["dev"], torch, 10), 5),
+                                 "cold_baseline_ms": round(cold_times(bops[1][1], r["dev"], torch, 10), 5)}
+            res["clock"] = clock_under_load(bops[0][1], r["dev"], torch)
+            for _, op in bops:
+                op.close()
+            res["baseline_parts"] = baseline_parts(w, r["dev"], torch, A)
         ym = yardstick_matmul(w, r["dev"], args.steps, args.warmup, torch)
         res["yardstick_torch_matmul_pregathered"] = {
             "median_ms": round(ym, 5), "tflops": round(tflops(w.M, w.N, w.K, ym / 1e3), 3)}

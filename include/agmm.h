@@ -367,6 +367,17 @@ int ag_matmul_plan_query(const agmm_desc* desc, int num_cus, int what, void* dst
  * staging) on `hip_stream`. */
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream);
 
+/* Measurement of the barrier baseline's two phases on their own: for a handle with
+ * algo = AGMM_ALGO_BASELINE (and no gather_a), enqueues only the staging copy
+ * (AGMM_PART_COPY: every staged unit of A into the staging buffer, [M][K]) or only the GEMM
+ * over the staging buffer as it stands (AGMM_PART_GEMM), with the arguments of
+ * ag_matmul_run. A GEMM part's output is the op's only once a copy part has run on the same
+ * inputs. Returns the codes of ag_matmul_run; INVALID_ARG for another kind of handle or part. */
+#define AGMM_PART_COPY 1
+#define AGMM_PART_GEMM 2
+int ag_matmul_debug_run_part(agmm_handle* h, int part, const void* const* shards, const void* B,
+                             const void* bias, void* out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif
