@@ -56,6 +56,8 @@ class agmm_desc(ctypes.Structure):
         ("trace_cap", ctypes.c_int32), ("spin_limit", ctypes.c_uint32),
         ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
         ("gather_a", ctypes.c_int32), ("pipeline_chunks", ctypes.c_int32),
+        ("debug_fetch_delay", ctypes.c_int32), ("debug_fetch_seed", ctypes.c_uint32),
+        ("debug_fetch_reverse", ctypes.c_int32),
     ]
 
 

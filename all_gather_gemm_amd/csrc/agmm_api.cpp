@@ -114,6 +114,7 @@ int validate_desc(const agmm_desc* d) {
   if (d->debug_skip_unit < -1) return AGMM_ERR_INVALID_ARG;
   if (d->tail_split != 0 && d->tail_split != 1) return AGMM_ERR_INVALID_ARG;
   if (d->gather_a != 0 && d->gather_a != 1) return AGMM_ERR_INVALID_ARG;
+  if (d->debug_fetch_delay < 0 || (d->debug_fetch_reverse & ~1)) return AGMM_ERR_INVALID_ARG;
   if (d->gather_a && d->layout != AGMM_K_CONTIGUOUS) return AGMM_ERR_UNSUPPORTED;
   if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
   if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
@@ -585,7 +586,15 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
     // the kernels copy a recorded timeout to the host word through its device address
     void* dptr = nullptr;
     if ((e = hipHostGetDevicePointer(&dptr, h->host_status, 0)) != hipSuccess) return fail(e);
-    const uint32_t words[2] = {(uint32_t)(uintptr_t)dptr, (uint32_t)((uint64_t)(uintptr_t)dptr >> 32)};
+    const uint32_t words[5] = {(uint32_t)(uintptr_t)dptr,
+                               (uint32_t)((uint64_t)(uintptr_t)dptr >> 32),
+                               (uint32_t)desc->debug_fetch_delay, desc->debug_fetch_seed,
+                               (uint32_t)desc->debug_fetch_reverse};
+    static_assert(agmm::CTR_HOST_HI == agmm::CTR_HOST_LO + 1 &&
+                      agmm::CTR_DBG_DELAY == agmm::CTR_HOST_LO + 2 &&
+                      agmm::CTR_DBG_SEED == agmm::CTR_HOST_LO + 3 &&
+                      agmm::CTR_DBG_REVERSE == agmm::CTR_HOST_LO + 4,
+                  "the words written together are contiguous");
     if ((e = hipMemcpy(h->ctr + agmm::CTR_HOST_LO, words, sizeof(words), hipMemcpyHostToDevice)) !=
         hipSuccess)
       return fail(e);
@@ -1192,7 +1201,8 @@ int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const
                          const void* bias, void* out, void* hip_stream) {
   int rc = validate_desc(desc);
   if (rc != AGMM_OK) return rc;
-  if (desc->algo == AGMM_ALGO_PIPELINED || desc->gather_a || desc->debug || desc->tail_split)
+  if (desc->algo == AGMM_ALGO_PIPELINED || desc->gather_a || desc->debug || desc->tail_split ||
+      desc->debug_fetch_delay || desc->debug_fetch_reverse)
     return AGMM_ERR_UNSUPPORTED;
   int dev = 0;
   AGMM_HIP(hipGetDevice(&dev));

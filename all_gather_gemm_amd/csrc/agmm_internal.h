@@ -37,6 +37,9 @@ enum : int {
   CTR_STATUS_SEEN = 5,  // flag value it last saw
   CTR_HOST_LO = 6,      // device address of the handle's host-visible status mirror
   CTR_HOST_HI = 7,      // (uint32[4], pinned host memory), low and high words; 0 = none
+  CTR_DBG_DELAY = 8,    // fetch stress knobs, written at create: max back-off steps before
+  CTR_DBG_SEED = 9,     // a unit's copy (0 = none), the seed of the per-unit delay hash,
+  CTR_DBG_REVERSE = 10, // and 1 = claim units in reverse fetch order
   CTR_FETCH = 64,       // next fetch unit to claim (own 128-byte line)
   CTR_Q = 96,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
   CTR_QSTRIDE = 32,

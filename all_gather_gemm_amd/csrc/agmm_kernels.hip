@@ -1132,6 +1132,16 @@ __device__ __attribute__((always_inline)) void fetch_unit(const KParams& p,
   const int KG = p.kpf * T::BK;
   const uint64_t t0 = tr.now();
   const int t_m = (int)p.units[2 * u], g = (int)p.units[2 * u + 1];
+  // stress knob: a per-unit delay from a hash of (unit, seed), so that units complete out of
+  // their fetch order (every wave sleeps the same count: the value is workgroup-uniform)
+  const uint32_t max_delay = uniform32(p.ctr[CTR_DBG_DELAY]);
+  if (max_delay) {
+    uint32_t h = (uint32_t)u * 0x9E3779B1u ^ uniform32(p.ctr[CTR_DBG_SEED]);
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    for (uint32_t i = h % max_delay; i > 0; --i) __builtin_amdgcn_s_sleep(2);
+  }
   if (LAYOUT_K)
     copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
   else
@@ -1149,9 +1159,13 @@ __device__ __attribute__((always_inline)) void fetch_unit(const KParams& p,
 // Claims the next fetch unit for the workgroup (>= p.num_units: none left). slot: an LDS
 // word; the caller's next claim comes after a barrier (fetch_unit has one).
 __device__ inline int claim_unit(const KParams& p, int* slot, int tid) {
-  if (tid == 0)
-    *slot = aborted(p) ? p.num_units
+  if (tid == 0) {
+    int u = aborted(p) ? p.num_units
                        : (int)min((uint32_t)p.num_units, atomicAdd(p.ctr + CTR_FETCH, 1u));
+    // stress knob: the n-th claim takes unit num_units - 1 - n (still each unit once)
+    if (u < p.num_units && p.ctr[CTR_DBG_REVERSE]) u = p.num_units - 1 - u;
+    *slot = u;
+  }
   __syncthreads();
   return __builtin_amdgcn_readfirstlane(*slot);
 }

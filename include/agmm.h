@@ -114,6 +114,14 @@ typedef struct agmm_desc {
   int32_t pipeline_chunks; /* AGMM_ALGO_PIPELINED: chunks S per shard; 0 = auto (4). Lowered
                               to the largest S with M/D a multiple of S * block_m (1 when
                               M/D is not a multiple of block_m) */
+  /* Stress knobs for the fused fetch (tests of the flag protocol; results must not change):
+   * before copying unit u a fetcher sleeps hash(u, seed) % debug_fetch_delay back-off steps
+   * (s_sleep 2, about 128 clocks each; 0 = no delay), and with debug_fetch_reverse = 1 the
+   * n-th unit claimed is unit num_units - 1 - n of the fetch order (the units the first
+   * tiles need come last). */
+  int32_t debug_fetch_delay;
+  uint32_t debug_fetch_seed;
+  int32_t debug_fetch_reverse;
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
@@ -217,8 +225,8 @@ int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* 
  * array of the library (80 MiB, held by each device the library has run this on until the
  * process ends; its address is looked up once per device); the caller still passes inputs
  * and outputs exactly as for ag_matmul_run, on the current device.
- *   desc: as for ag_matmul_create; algo FUSED or BASELINE; debug, gather_a and tail_split
- *         must be 0 (UNSUPPORTED otherwise). The workspace create would use for it,
+ *   desc: as for ag_matmul_create; algo FUSED or BASELINE; debug, gather_a, tail_split and
+ *         the fetch stress knobs must be 0 (UNSUPPORTED otherwise). The workspace create would use for it,
  *         ag_matmul_workspace_bytes(desc) on this device, must fit the scratch, else
  *         TOO_LARGE and nothing is enqueued: a staging buffer of up to 64 MiB, e.g.
  *         4096 x 8192 16-bit elements of A.
