@@ -40,7 +40,7 @@ EXPORTED = [
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
     "ag_gemm_ar_flags_plan", "ag_matmul_sync_status", "ag_matmul_run_static",
-    "ag_matmul_debug_run_part",
+    "ag_matmul_debug_run_part", "ag_matmul_debug_mfma_loop",
 ]
 PART_COPY, PART_GEMM = 1, 2
 
@@ -116,6 +116,8 @@ def _load():
                                      ctypes.POINTER(vp)]
     lib.ag_matmul_sync_status.argtypes = [vp]
     lib.ag_matmul_debug_run_part.argtypes = [vp, ctypes.c_int, ctypes.POINTER(vp), vp, vp, vp, vp]
+    lib.ag_matmul_debug_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, vp, vp]
     lib.ag_matmul_run_static.argtypes = [ctypes.POINTER(agmm_desc), ctypes.POINTER(vp), vp, vp,
                                          vp, vp]
     lib.ag_matmul_run.argtypes = [vp, ctypes.POINTER(vp), vp, vp, vp, vp]
@@ -232,6 +234,12 @@ def ag_matmul_debug_run_part(handle: int, part: int, shard_ptrs: Sequence[int], 
     return lib.ag_matmul_debug_run_part(ctypes.c_void_p(handle), part, arr, ctypes.c_void_p(B_ptr),
                                         ctypes.c_void_p(bias_ptr) if bias_ptr else None,
                                         ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream))
+
+
+def ag_matmul_debug_mfma_loop(dtype: int, vary: bool, grid: int, iters: int, sink_ptr: int,
+                              stream: int = 0) -> int:
+    return lib.ag_matmul_debug_mfma_loop(dtype, int(vary), grid, iters, ctypes.c_void_p(sink_ptr),
+                                         ctypes.c_void_p(stream))
 
 
 def ag_matmul_sync_status(handle: int) -> int:

@@ -58,13 +58,27 @@ def _gfx950_code_object(obj: str) -> bytes:
 
 def kernel_resources(obj: str) -> dict:
     """Registers, spills and LDS of every kernel in obj's gfx950 code object, from its
-    metadata note, with the code object's sha256."""
+    metadata note, the sha256 of each kernel's machine code, and the code object's sha256."""
     co = _gfx950_code_object(obj)
     with tempfile.NamedTemporaryFile(suffix=".co") as fh:
         fh.write(co)
         fh.flush()
         notes = subprocess.run([os.path.join(LLVM_BIN, "llvm-readelf"), "--notes", fh.name],
                                check=True, capture_output=True, text=True).stdout
+        syms = subprocess.run([os.path.join(LLVM_BIN, "llvm-readelf"), "--symbols", "--wide",
+                               "--sections", fh.name], check=True, capture_output=True,
+                              text=True).stdout
+    # the machine code of each kernel: its symbol's bytes in .text (address - section address
+    # + section file offset)
+    text = re.search(r"\]\s+\.text\s+PROGBITS\s+([0-9a-f]+)\s+([0-9a-f]+)\s+([0-9a-f]+)", syms)
+    code = {}
+    if text:
+        t_addr, t_off = int(text.group(1), 16), int(text.group(2), 16)
+        for m in re.finditer(r"^\s*\d+:\s+([0-9a-f]+)\s+(\d+)\s+FUNC\s+\S+\s+\S+\s+\S+\s+(\S+)$",
+                             syms, re.M):
+            addr, size, name = int(m.group(1), 16), int(m.group(2)), m.group(3)
+            off = addr - t_addr + t_off
+            code[name] = hashlib.sha256(co[off:off + size]).hexdigest()
     kernels = {}
     for block in notes.split("\n  - ")[1:]:
         name = re.search(r"\.name:\s+(\S+)", block)
@@ -75,6 +89,8 @@ def kernel_resources(obj: str) -> dict:
             m = re.search(r"\." + f + r":\s+(\d+)", block)
             if m:
                 rec[f] = int(m.group(1))
+        if name.group(1) in code:
+            rec["code_sha256"] = code[name.group(1)]
         kernels[name.group(1)] = rec
     return {"code_object_sha256": hashlib.sha256(co).hexdigest(), "kernels": kernels}
 

@@ -1248,6 +1248,15 @@ int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const
   return run_impl(&h, shards, B, bias, out, false, nullptr, hip_stream);
 }
 
+int ag_matmul_debug_mfma_loop(int dtype, int vary, int grid, int iters, float* sink,
+                              void* hip_stream) {
+  if (dtype != AGMM_F16 && dtype != AGMM_BF16) return AGMM_ERR_INVALID_ARG;
+  if (!sink || grid <= 0 || iters <= 0 || (iters & 3) || (vary & ~1)) return AGMM_ERR_INVALID_ARG;
+  AGMM_HIP(agmm::launch_mfma_loop(dtype, vary != 0, grid, iters, sink,
+                                  reinterpret_cast<hipStream_t>(hip_stream)));
+  return AGMM_OK;
+}
+
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {
   if (!h) return AGMM_ERR_INVALID_ARG;
   int cur = 0;

@@ -104,6 +104,10 @@ hipError_t launch_ar_flags(const KParams& p, int dtype, int block_m, int grid, h
 hipError_t launch_ar_finalize(const float* C, const uint16_t* bias, uint16_t* out, int64_t M,
                               int64_t N, int dtype, hipStream_t s);
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s);
+// Measurement: grid workgroups of 4 waves, each running iters x 16 32x32x16 MFMAs on
+// pseudo-random register operands (vary: rotating through 4 sets; else one set); writes
+// grid * 256 floats to sink. iters a positive multiple of 4.
+hipError_t launch_mfma_loop(int dtype, bool vary, int grid, int iters, float* sink, hipStream_t s);
 hipError_t launch_fill32(uint32_t* dst, int64_t n, uint32_t v, hipStream_t s);
 // Resident workgroups per CU for the fused kernel of this family (occupancy query).
 hipError_t fused_occupancy(int dtype, int block_m, int* per_cu);

@@ -1374,6 +1374,50 @@ __global__ __launch_bounds__(kUploadWords) void upload32_kernel(uint32_t* dst, U
   if (i < p.n) dst[i] = p.w[i];
 }
 
+// Measurement only: the MFMA rate this GPU sustains with operands held in registers (no
+// memory traffic in the loop). Every wave runs 16 independent 32x32x16 accumulators on
+// pseudo-random 16-bit operands (random signs and mantissas, like real data); with VARY they
+// rotate through four register sets, otherwise one set is reused. One float per thread is
+// written so the loop is not removed.
+template <int DT, bool VARY>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(float* sink, int iters) {
+  u32x4 av[4], bv[4];
+  uint32_t h = threadIdx.x * 2654435761u + blockIdx.x * 40503u + 12345u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        h ^= h << 13;
+        h ^= h >> 17;
+        h ^= h << 5;
+        // a finite 16-bit value in [-1, 1): random mantissa and sign, small exponent
+        x[j] = Num<DT>::to_bits(((int)(h & 0xffffu) - 32768) * (1.0f / 32768.0f));
+      }
+      av[r][i] = x[0] | (x[1] << 16);
+      bv[r][i] = (x[0] ^ 0x5a5au) | ((x[1] ^ 0x3c3cu) << 16);
+    }
+  f32x16 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = (f32x16)(0.0f);
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[j] = Num<DT>::mfma(VARY ? av[(r + j) & 3] : av[0], VARY ? bv[(3 * r + j) & 3] : bv[0],
+                               acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += acc[j][k];
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 __global__ void fill16_kernel(uint16_t* dst, int64_t n, uint16_t v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -1544,6 +1588,19 @@ hipError_t launch_upload32(uint32_t* dst, const uint32_t* src, int64_t n, hipStr
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_mfma_loop(int dtype, bool vary, int grid, int iters, float* sink,
+                            hipStream_t s) {
+  if (grid <= 0 || iters <= 0 || (iters & 3)) return hipErrorInvalidValue;
+  if (dtype == AGMM_BF16) {
+    if (vary) hipLaunchKernelGGL((mfma_loop_kernel<AGMM_BF16, true>), dim3(grid), dim3(256), 0, s, sink, iters);
+    else hipLaunchKernelGGL((mfma_loop_kernel<AGMM_BF16, false>), dim3(grid), dim3(256), 0, s, sink, iters);
+  } else {
+    if (vary) hipLaunchKernelGGL((mfma_loop_kernel<AGMM_F16, true>), dim3(grid), dim3(256), 0, s, sink, iters);
+    else hipLaunchKernelGGL((mfma_loop_kernel<AGMM_F16, false>), dim3(grid), dim3(256), 0, s, sink, iters);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fill16(uint16_t* dst, int64_t n, uint16_t v, hipStream_t s) {

@@ -249,8 +249,9 @@ def kernel_entry(res, block_m, dtype, fused, layout_k, row_wait):
 
 def measured_traffic(workload_name, algo):
     """HBM bytes per launch of the fused kernel from the committed counter summary (rocprofv3
-    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when that summary was taken on another
-    build (the code object hash it records differs from the built one) or another workload."""
+    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when that summary was taken on other
+    machine code (the hash of the fused kernel's instructions it records differs from the
+    built kernel's) or another workload."""
     if workload_name != "ag_16384x3584x8192_d8_f16_bias" or algo != "fused":
         return None
     res = kernel_resources()
@@ -265,7 +266,8 @@ def measured_traffic(workload_name, algo):
                     kv[k.strip()] = v.strip()
     except OSError:
         return None
-    if kv.get("code_object_sha256") != res["code_object_sha256"]:
+    ent = kernel_entry(res, 256, "f16", True, False, False)
+    if not ent or kv.get("kernel_code_sha256") != ent.get("code_sha256"):
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -365,6 +367,34 @@ def baseline_parts(w, dev, torch, A, reps=20):
             "copy_frac_of_hbm_peak": round(staged / (out["copy_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_ms": round(out["gemm_ms"], 5),
             "gemm_tflops": round(tflops(w.M, w.N, w.K, out["gemm_ms"] * 1e-3), 1)}
+
+
+def mfma_ceiling(torch, A, iters=20000):
+    """TFLOP/s of a register-only MFMA loop (ag_matmul_debug_mfma_loop), fp16, per grid size
+    and operand kind, best of 3 launches: the rate the chip sustains with no memory traffic, at
+    the clock its power limit allows for that switching activity."""
+    sink = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for vary in (False, True):
+        for grid in (64, 256, 512):
+            A.ag_matmul_debug_mfma_loop(A.F16, vary, grid, 2000, sink.data_ptr(), s)
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rc = A.ag_matmul_debug_mfma_loop(A.F16, vary, grid, iters, sink.data_ptr(), s)
+                e1.record()
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"ag_matmul_debug_mfma_loop: {rc}")
+                ms = e0.elapsed_time(e1)
+                tf = grid * 4 * iters * 16 * 32768.0 / (ms * 1e-3) / 1e12
+                best = tf if best is None else max(best, tf)
+            res[f"{'rotating' if vary else 'fixed'}_operands_grid{grid}_tflops"] = round(best, 1)
+    res["peak_tflops"] = PEAK_TFLOPS["f16"]
+    return res
 
 
 def timeline(w, torch, A, runs=3, **tun):
@@ -479,6 +509,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="only print the fused kernel's fetch/GEMM timeline from a debug trace "
                          "(for each of --workload, or of all five workloads with --sweep)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the MFMA rate with pseudo-random register operands (no "
+                         "memory traffic), one set or four rotating, on 64, 256 and 512 workgroups")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the "
                          "known-size reference for the HBM byte counters")
@@ -507,6 +540,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
                           "dispatches": 3}), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling(torch, A)), flush=True)
         return
     if args.timeline:
         for w in (WORKLOADS if args.sweep else [BY_NAME[args.workload]]):

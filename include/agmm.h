@@ -386,6 +386,16 @@ int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_str
 int ag_matmul_debug_run_part(agmm_handle* h, int part, const void* const* shards, const void* B,
                              const void* bias, void* out, void* hip_stream);
 
+/* Measurement of the MFMA ceiling (no memory traffic): enqueues `grid` workgroups of 256
+ * threads, each wave running iters x 16 v_mfma_f32_32x32x16 (dtype AGMM_F16 or AGMM_BF16) on
+ * register operands, i.e. grid * 4 * iters * 16 * 32768 FLOP, the operands pseudo-random
+ * 16-bit values (random signs and mantissas, like real data); vary = 1 rotates them through
+ * four register sets, 0 reuses one set. sink: device float[grid * 256], written. iters > 0, a
+ * multiple of 4.
+ * Returns AGMM_OK, INVALID_ARG or HIP. */
+int ag_matmul_debug_mfma_loop(int dtype, int vary, int grid, int iters, float* sink,
+                              void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif
