@@ -57,7 +57,7 @@ class agmm_desc(ctypes.Structure):
         ("debug_skip_unit", ctypes.c_int32), ("tail_split", ctypes.c_int32),
         ("gather_a", ctypes.c_int32), ("pipeline_chunks", ctypes.c_int32),
         ("debug_fetch_delay", ctypes.c_int32), ("debug_fetch_seed", ctypes.c_uint32),
-        ("debug_fetch_reverse", ctypes.c_int32),
+        ("debug_fetch_reverse", ctypes.c_int32), ("fetch_kernel", ctypes.c_int32),
     ]
 
 
@@ -73,7 +73,7 @@ class agmm_config(ctypes.Structure):
         ("num_cus", ctypes.c_int32), ("split_tiles", ctypes.c_int32),
         ("split_pieces", ctypes.c_int32), ("num_items", ctypes.c_int32),
         ("row_wait", ctypes.c_int32), ("pipeline_chunks", ctypes.c_int32),
-        ("pipeline_streams", ctypes.c_int32),
+        ("pipeline_streams", ctypes.c_int32), ("fetch_kernel", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -434,8 +434,10 @@ class AgMatmul:
         return ag_matmul_sync_status(self.handle)
 
     def trace(self):
+        """Per-workgroup trace counts and records: the persistent grid's workgroups, then (with
+        a fetch kernel) the fetch kernel's."""
         c = self.config
-        W = c.num_wgs
+        W = c.num_wgs + (c.num_fetch_wgs if c.fetch_kernel else 0)
         counts = np.frombuffer(ag_matmul_debug_query(self.handle, Q_TRACE_COUNT, W * 4), dtype="<u4")
         recs = np.frombuffer(ag_matmul_debug_query(self.handle, Q_TRACE,
                                                    W * c.trace_cap * TRACE_DTYPE.itemsize),

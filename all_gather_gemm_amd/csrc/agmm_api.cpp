@@ -51,6 +51,11 @@ struct agmm_handle {
   hipStream_t pstreams[kPipeStreams - 1];  // streams 1 .. of the rotation
   hipEvent_t ev_start, ev_done[kPipeStreams - 1];
   int n_pstreams, n_events;  // created so far (destroy releases these)
+  // fetch kernel (cfg.fetch_kernel): its stream, and the events that order it after the work
+  // before a run on the caller's stream (ev_fin) and that stream after it (ev_fout)
+  hipStream_t fstream;
+  hipEvent_t ev_fin, ev_fout;
+  bool has_fstream, has_fev;
   // GEMM + all-reduce handles (ag_gemm_ar_create): ranks and this rank; 0 otherwise
   int32_t ar_D, ar_rank;
   // ag_gemm_ar_flags_create: every rank's share in one launch. A second device allocation
@@ -115,6 +120,7 @@ int validate_desc(const agmm_desc* d) {
   if (d->tail_split != 0 && d->tail_split != 1) return AGMM_ERR_INVALID_ARG;
   if (d->gather_a != 0 && d->gather_a != 1) return AGMM_ERR_INVALID_ARG;
   if (d->debug_fetch_delay < 0 || (d->debug_fetch_reverse & ~1)) return AGMM_ERR_INVALID_ARG;
+  if (d->fetch_kernel < -1 || d->fetch_kernel > 1) return AGMM_ERR_INVALID_ARG;
   if (d->gather_a && d->layout != AGMM_K_CONTIGUOUS) return AGMM_ERR_UNSUPPORTED;
   if (d->N % 8 != 0 || d->K % 8 != 0) return AGMM_ERR_UNSUPPORTED;
   if (d->layout == AGMM_M_CONTIGUOUS && d->algo == AGMM_ALGO_FUSED && d->M % 8 != 0)
@@ -284,22 +290,34 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   // workgroups than that are left over: then every fetcher would hold back a tile for the
   // whole fetch, and one fetcher per unit finishes the fetch in one pass instead.
   int F = 0;
-  if (n_units > 0) {
-    F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
-    if (!d.num_fetch_wgs && c.num_items <= W_base && W_base - c.num_items < kDefaultFetchWgs)
-      F = (int)std::min<int64_t>(n_units, W_base);
+  int64_t W = W_base;
+  c.fetch_kernel = (d.algo == AGMM_ALGO_FUSED && n_units > 0 && d.fetch_kernel == 1) ? 1 : 0;
+  if (c.fetch_kernel) {
+    // Fetch kernel beside the grid: F of its workgroups (one per CU by default, none idle),
+    // and every grid workgroup computes. Its units arrive over the GEMM's first K steps, so
+    // the K loop waits for each staged k-group as it reaches it.
+    F = (int)std::min<int64_t>(d.num_fetch_wgs ? d.num_fetch_wgs : num_cus, n_units);
+    W = std::max<int64_t>(1, std::min<int64_t>(W_base, c.num_items));
+    c.num_fetch_wgs = F;
+    c.num_wgs = (int32_t)W;
+    c.row_wait = 0;
+  } else {
+    if (n_units > 0) {
+      F = d.num_fetch_wgs ? d.num_fetch_wgs : kDefaultFetchWgs;
+      if (!d.num_fetch_wgs && c.num_items <= W_base && W_base - c.num_items < kDefaultFetchWgs)
+        F = (int)std::min<int64_t>(n_units, W_base);
+    }
+    F = (int)std::min<int64_t>(F, n_units);
+    W = std::min<int64_t>(W, (int64_t)F + c.num_items);  // every workgroup resident, none idle
+    F = (int)std::min<int64_t>(F, W);
+    if (c.num_tiles > 0 && W < 1) W = 1;
+    c.num_fetch_wgs = F;
+    c.num_wgs = (int32_t)W;
+    // Every unit has a fetcher of its own: the fetch is one pass, so tiles wait for their
+    // whole row at their start and run a K loop without polls (measured faster than
+    // per-k-group waits in that case, and slower when fetchers take several units each).
+    c.row_wait = (n_units > 0 && F >= n_units) ? 1 : 0;
   }
-  F = (int)std::min<int64_t>(F, n_units);
-  int64_t W = W_base;                                  // every workgroup resident
-  W = std::min<int64_t>(W, (int64_t)F + c.num_items);  // no idle workgroups
-  F = (int)std::min<int64_t>(F, W);
-  if (c.num_tiles > 0 && W < 1) W = 1;
-  c.num_fetch_wgs = F;
-  c.num_wgs = (int32_t)W;
-  // Every unit has a fetcher of its own: the fetch is one pass, so tiles wait for their whole
-  // row at their start and run a K loop without polls (measured faster than per-k-group
-  // waits in that case, and slower when fetchers take several units each).
-  c.row_wait = (n_units > 0 && F >= n_units) ? 1 : 0;
   c.num_copy_wgs = (int32_t)std::min<int64_t>(n_units, 4LL * num_cus);
 
   make_queues(T_m, T_n, pl->mtiles, S, pl);
@@ -390,7 +408,8 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   }
 
   c.trace_cap = d.debug ? (d.trace_cap ? d.trace_cap : kDefaultTraceCap) : 0;
-  pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) : 0;
+  // debug trace: the grid's workgroups, then the fetch kernel's
+  pl->trace_wgs = d.debug ? std::max<int64_t>(W, 1) + (c.fetch_kernel ? F : 0) : 0;
   c.staging_elems = (n_units > 0 && !d.gather_a) ? d.M * d.K : 0;
   pl->flags_n = std::max<int64_t>(1, T_m * G);
 
@@ -474,6 +493,12 @@ void release_streams(agmm_handle* h) {
   for (int j = 0; j + 1 < h->n_events; ++j) (void)hipEventDestroy(h->ev_done[j]);
   h->n_pstreams = 0;
   h->n_events = 0;
+  if (h->has_fstream) (void)hipStreamDestroy(h->fstream);
+  if (h->has_fev) {
+    (void)hipEventDestroy(h->ev_fin);
+    (void)hipEventDestroy(h->ev_fout);
+  }
+  h->has_fstream = h->has_fev = false;
 }
 
 }  // namespace
@@ -535,12 +560,19 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
   int per_cu = 0;
   AGMM_HIP(agmm::fused_occupancy(desc->dtype, pl.cfg.block_m, &per_cu));
   if (per_cu < 1) return AGMM_ERR_UNSUPPORTED;
+  if (pl.cfg.fetch_kernel) {
+    bool fits = false;
+    AGMM_HIP(agmm::fetch_fits_beside(desc->dtype, pl.cfg.block_m,
+                                     desc->layout == AGMM_K_CONTIGUOUS, &fits));
+    if (!fits) return AGMM_ERR_UNSUPPORTED;
+  }
 
   agmm_handle* h = new (std::nothrow) agmm_handle();
   if (!h) return AGMM_ERR_OOM;
   init_handle(h, *desc, pl, dev);
   h->n_pstreams = 0;
   h->n_events = 0;
+  h->has_fstream = h->has_fev = false;
   if (workspace && workspace_bytes < (size_t)pl.total) {
     delete h;
     return AGMM_ERR_INVALID_ARG;
@@ -636,6 +668,19 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
         return fail(e);
       ++h->n_events;
     }
+  }
+  if (pl.cfg.fetch_kernel) {
+    // a default-priority stream that does not synchronize with the null stream
+    if ((e = hipStreamCreateWithFlags(&h->fstream, hipStreamNonBlocking)) != hipSuccess)
+      return fail(e);
+    h->has_fstream = true;
+    if ((e = hipEventCreateWithFlags(&h->ev_fin, hipEventDisableTiming)) != hipSuccess)
+      return fail(e);
+    if ((e = hipEventCreateWithFlags(&h->ev_fout, hipEventDisableTiming)) != hipSuccess) {
+      (void)hipEventDestroy(h->ev_fin);
+      return fail(e);
+    }
+    h->has_fev = true;
   }
   if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
   *out_handle = h;
@@ -814,7 +859,23 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   KParams p = run_params(h, shards, B, bias, out,
                           d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging, epoch);
 
-  if (d.algo == AGMM_ALGO_FUSED) {
+  if (d.algo == AGMM_ALGO_FUSED && c.fetch_kernel) {
+    // The fetch kernel on the handle's stream, after the caller's stream reaches this point;
+    // the GEMM grid (no fetchers) on the caller's stream; the caller's stream then waits for
+    // the fetch kernel, so the run ends when both have.
+    p.F = 0;
+    p.staged_kmajor = d.layout == AGMM_K_CONTIGUOUS ? 1 : 0;
+    p.row_wait = c.row_wait;
+    KParams q = p;
+    if (p.trace) q.trace = p.trace + (size_t)c.num_wgs * c.trace_cap;
+    q.trace_count = p.trace_count + c.num_wgs;
+    AGMM_HIP(hipEventRecord(h->ev_fin, s));
+    AGMM_HIP(hipStreamWaitEvent(h->fstream, h->ev_fin, 0));
+    AGMM_HIP(agmm::launch_fetch(q, c.block_m, p.staged_kmajor != 0, c.num_fetch_wgs, h->fstream));
+    AGMM_HIP(agmm::launch_fused(p, d.dtype, c.block_m, c.num_wgs, s));
+    AGMM_HIP(hipEventRecord(h->ev_fout, h->fstream));
+    AGMM_HIP(hipStreamWaitEvent(s, h->ev_fout, 0));
+  } else if (d.algo == AGMM_ALGO_FUSED) {
     p.F = c.num_fetch_wgs;
     p.staged_kmajor = d.layout == AGMM_K_CONTIGUOUS ? 1 : 0;
     p.row_wait = c.row_wait;
@@ -856,8 +917,7 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   } else {
     p.F = 0;
     p.staged_kmajor = 1;  // the baseline gathers into plain [M][K] rows
-    p.debug = 0;
-    p.trace_cap = 0;
+    // debug: the GEMM kernel records its tiles in the trace like the fused kernel does
     if (c.num_units > 0 && part != AGMM_PART_GEMM)
       AGMM_HIP(agmm::launch_copy(p, c.block_m, c.num_copy_wgs, s));
     const int grid = (int)std::min<int64_t>(std::min(c.num_cus, c.num_items),
@@ -1201,8 +1261,9 @@ int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const
                          const void* bias, void* out, void* hip_stream) {
   int rc = validate_desc(desc);
   if (rc != AGMM_OK) return rc;
+  // (a fetch kernel would need a stream of its own, which this entry point cannot create)
   if (desc->algo == AGMM_ALGO_PIPELINED || desc->gather_a || desc->debug || desc->tail_split ||
-      desc->debug_fetch_delay || desc->debug_fetch_reverse)
+      desc->debug_fetch_delay || desc->debug_fetch_reverse || desc->fetch_kernel == 1)
     return AGMM_ERR_UNSUPPORTED;
   int dev = 0;
   AGMM_HIP(hipGetDevice(&dev));

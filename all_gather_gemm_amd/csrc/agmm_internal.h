@@ -40,6 +40,7 @@ enum : int {
   CTR_DBG_DELAY = 8,    // fetch stress knobs, written at create: max back-off steps before
   CTR_DBG_SEED = 9,     // a unit's copy (0 = none), the seed of the per-unit delay hash,
   CTR_DBG_REVERSE = 10, // and 1 = claim units in reverse fetch order
+  CTR_FDONE = 32,       // fetch-kernel workgroups that finished (own 128-byte line)
   CTR_FETCH = 64,       // next fetch unit to claim (own 128-byte line)
   CTR_Q = 96,           // queue x counter at CTR_Q + x * CTR_QSTRIDE
   CTR_QSTRIDE = 32,
@@ -95,6 +96,12 @@ static_assert(sizeof(KParams) == 1312, "kernel argument block size");
 hipError_t launch_fused(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 hipError_t launch_gemm_only(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s);
+// The fetch kernel (fused grid without fetchers beside it, on another stream): grid
+// workgroups claim and publish the units of p.units. layout_k: k_contiguous staging.
+hipError_t launch_fetch(const KParams& p, int block_m, bool layout_k, int grid, hipStream_t s);
+// Whether a fetch-kernel workgroup fits on a CU beside a fused GEMM workgroup of this tile
+// family (registers per SIMD and LDS per CU, from the kernels' own attributes).
+hipError_t fetch_fits_beside(int dtype, int block_m, bool layout_k, bool* fits);
 // The GEMM-only persistent kernel whose tiles are added (fp32 atomics) into p.ar_out[].
 hipError_t launch_gemm_ar(const KParams& p, int dtype, int block_m, int grid, hipStream_t s);
 // GEMM + all-reduce with per-tile flags, every rank's share in one launch: items in

@@ -945,9 +945,17 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
 // bandwidth, so the copies run as a two-batch software pipeline: the loads of batch n + 1
 // are issued before the stores of batch n, so neither waits for the other (a wait for
 // loads also waits for every store issued before them: the vector memory counter retires
-// in order). A batch is kCopyBatch 16-byte loads per thread (64 KiB per workgroup); at
-// most three batches of requests are in flight, within the counter's range of 63.
+// in order). A batch is BATCH 16-byte loads per thread (kCopyBatch: 64 KiB per workgroup);
+// at most three batches of requests are in flight, within the counter's range of 63. The
+// fetch kernel that runs beside the GEMM kernel takes kSmallCopyBatch, so that its data
+// registers (two batches) fit in what a GEMM wave leaves of a SIMD's register file
+// (8 for the m_contiguous copy, whole 8x8 blocks; 4 for the k_contiguous one, whose GEMM
+// waves take 16 registers more and which also keeps an offset per load).
 constexpr int kCopyBatch = 16;
+template <bool LAYOUT_K>
+constexpr int kSmallCopyBatch = LAYOUT_K ? 4 : 8;
+// VGPRs per lane the fetch kernel may use (its two instances' attributes): 512 minus the
+// GEMM waves' allocation, 424 with m_contiguous staging and 440 with k_contiguous.
 
 // Source row pointers of one unit: rows m_beg .. m_beg + R - 1 of the gathered A. A unit
 // inside one shard (the usual case) needs no per-row shard lookup.
@@ -971,7 +979,7 @@ struct UnitRows {
 // shard (the usual case) the loads and stores are range-checked buffer accesses: a lane
 // past the unit reads zero and its store is dropped, so every thread runs the same number
 // of batches and the pipeline has no per-lane branch.
-template <int BM>
+template <int BM, int BATCH = kCopyBatch>
 __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid, int row0, int nrows) {
   const int64_t m_beg = (int64_t)t_m * BM + row0;
@@ -986,12 +994,12 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
   if (rows.base && span <= 0x7fffffffll) {
     const rsrc_t src = make_rsrc(rows.base, span);
     const rsrc_t dst = make_rsrc(p.staging + m_beg * p.K, span);
-    const int batches = (R * CR + kThreads * kCopyBatch - 1) / (kThreads * kCopyBatch);
-    u32x4 va[kCopyBatch], vb[kCopyBatch];
-    uint32_t oa[kCopyBatch], ob[kCopyBatch];
-    auto load = [&](u32x4 (&v)[kCopyBatch], uint32_t (&o)[kCopyBatch]) __attribute__((always_inline)) {
+    const int batches = (R * CR + kThreads * BATCH - 1) / (kThreads * BATCH);
+    u32x4 va[BATCH], vb[BATCH];
+    uint32_t oa[BATCH], ob[BATCH];
+    auto load = [&](u32x4 (&v)[BATCH], uint32_t (&o)[BATCH]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kCopyBatch; ++i) {
+      for (int i = 0; i < BATCH; ++i) {
         o[i] = r < R ? (uint32_t)(((int64_t)r * p.K + k_beg + cc * 8) * 2) : kOob;
         v[i] = bload16(src, o[i]);
         r += dr;
@@ -1002,9 +1010,9 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
         }
       }
     };
-    auto store = [&](const u32x4 (&v)[kCopyBatch], const uint32_t (&o)[kCopyBatch]) __attribute__((always_inline)) {
+    auto store = [&](const u32x4 (&v)[BATCH], const uint32_t (&o)[BATCH]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kCopyBatch; ++i) bstore16(dst, o[i], v[i]);
+      for (int i = 0; i < BATCH; ++i) bstore16(dst, o[i], v[i]);
     };
     load(va, oa);
     for (int n = 0; n < batches; n += 2) {
@@ -1033,10 +1041,11 @@ __device__ void copy_unit_kmajor(const KParams& p, const uint16_t* const* shards
 // b % 8 and mb = (b / 8) % NBM, so 8 consecutive lanes read 128 contiguous bytes of one row;
 // a thread's blocks b, b + 256, ... advance (kb, mb) by fixed steps (no division). Same
 // buffer-access fast path and pipeline as the k_contiguous copy.
-template <int BM>
+template <int BM, int BATCH = kCopyBatch>
 __device__ void copy_unit_mmajor(const KParams& p, const uint16_t* const* shards, int t_m, int g,
                                  int KG, int tid, int row0, int nrows) {
-  constexpr int NB = kCopyBatch / 8;  // blocks per thread and batch
+  static_assert(BATCH % 8 == 0, "whole 8x8 blocks per batch");
+  constexpr int NB = BATCH / 8;  // blocks per thread and batch
   const int64_t m_beg = (int64_t)t_m * BM + row0;
   const int R = (int)min((int64_t)nrows, p.M - m_beg);    // multiple of 8
   const int64_t k_beg = (int64_t)g * KG;
@@ -1125,7 +1134,7 @@ __device__ void copy_units(const KParams& p, const uint16_t* const* shards, int 
 // a workgroup barrier, and thread 0 adds 1 to the unit's flag with one agent-scope release
 // (a single L2 write-back for the workgroup instead of one per wave: a write-back flushes
 // the XCD's whole L2, which the GEMM workgroups beside this one are using).
-template <class T, bool LAYOUT_K>
+template <class T, bool LAYOUT_K, int BATCH = kCopyBatch>
 __device__ __attribute__((always_inline)) void fetch_unit(const KParams& p,
                                                           const uint16_t* const* shards, int u,
                                                           int tid, Tracer& tr) {
@@ -1142,10 +1151,10 @@ __device__ __attribute__((always_inline)) void fetch_unit(const KParams& p,
     h ^= h >> 12;
     for (uint32_t i = h % max_delay; i > 0; --i) __builtin_amdgcn_s_sleep(2);
   }
-  if (LAYOUT_K)
-    copy_unit_kmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
+  if constexpr (LAYOUT_K)
+    copy_unit_kmajor<T::BM, BATCH>(p, shards, t_m, g, KG, tid, 0, T::BM);
   else
-    copy_unit_mmajor<T::BM>(p, shards, t_m, g, KG, tid, 0, T::BM);
+    copy_unit_mmajor<T::BM, BATCH>(p, shards, t_m, g, KG, tid, 0, T::BM);
   wait_vmcnt<0>();
   __syncthreads();
   if (tid == 0) {
@@ -1253,7 +1262,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
       for (int x = 0; x < kQueueSlots; ++x)
         __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the unit counter only when this grid held the fetchers (a fetch kernel running
+      // beside it resets its own, and may still be claiming units nobody waits for)
+      if (p.F > 0)
+        __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       mirror_status(p);
     }
@@ -1368,6 +1380,46 @@ struct UploadWords {
   uint32_t n;
   uint32_t w[kUploadWords];
 };
+
+// The fetch as a kernel of its own, run on a second stream beside a fused GEMM grid that has
+// no fetchers (p.F == 0): its workgroups claim units from the same counter and publish them
+// exactly as in-kernel fetchers do. It needs no LDS beyond the claim slot and the shard
+// table, and few enough VGPRs per lane that one of its workgroups fits on a CU beside a
+// GEMM workgroup (which holds 424 or 440 of a SIMD's 512 registers per lane and 129 KiB of
+// the 160 KiB of LDS): the fetch then runs on every CU while every CU computes. Trace
+// records (debug) go to p.trace / p.trace_count, which the host offsets past the GEMM
+// grid's. The last workgroup out resets the unit counter for the next run.
+template <int BM, bool LAYOUT_K>
+__device__ __attribute__((always_inline)) void fetch_kernel_body(const KParams& p) {
+  using T = Tile<BM>;
+  __shared__ int s_claim;
+  __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
+  const int tid = threadIdx.x;
+  Tracer tr{p.debug ? p.trace + (size_t)blockIdx.x * p.trace_cap : nullptr, 0u,
+            (uint32_t)p.trace_cap, p.debug != 0};
+  load_shard_table(p, s_shards, tid);
+  for (;;) {
+    const int u = claim_unit(p, &s_claim, tid);
+    if (u >= p.num_units) break;
+    fetch_unit<T, LAYOUT_K, kSmallCopyBatch<LAYOUT_K>>(p, s_shards, u, tid, tr);
+  }
+  if (tid == 0) {
+    if (p.debug) p.trace_count[blockIdx.x] = tr.n;
+    const uint32_t old = atomicAdd(p.ctr + CTR_FDONE, 1u);
+    if (old == gridDim.x - 1) {
+      __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctr + CTR_FDONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+// m_contiguous staging: beside GEMM waves of 424 registers
+template <int BM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(88)))
+void agmm_fetch_m(KParams p) { fetch_kernel_body<BM, false>(p); }
+// k_contiguous staging: beside GEMM waves of 440 registers
+template <int BM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(72)))
+void agmm_fetch_k(KParams p) { fetch_kernel_body<BM, true>(p); }
 
 __global__ __launch_bounds__(kUploadWords) void upload32_kernel(uint32_t* dst, UploadWords p) {
   const uint32_t i = threadIdx.x;
@@ -1576,6 +1628,69 @@ hipError_t launch_copy(const KParams& p, int block_m, int grid, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fetch(const KParams& p, int block_m, bool layout_k, int grid, hipStream_t s) {
+  switch (block_m) {
+    case 256:
+      if (layout_k) hipLaunchKernelGGL(agmm_fetch_k<256>, dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(agmm_fetch_m<256>, dim3(grid), dim3(kThreads), 0, s, p);
+      break;
+    case 128:
+      if (layout_k) hipLaunchKernelGGL(agmm_fetch_k<128>, dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(agmm_fetch_m<128>, dim3(grid), dim3(kThreads), 0, s, p);
+      break;
+    case 64:
+      if (layout_k) hipLaunchKernelGGL(agmm_fetch_k<64>, dim3(grid), dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL(agmm_fetch_m<64>, dim3(grid), dim3(kThreads), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+namespace {
+// Registers per lane a wave is given (the allocation granule is 8) and static LDS bytes.
+hipError_t footprint(const void* k, int* regs, int* lds) {
+  hipFuncAttributes a;
+  const hipError_t e = hipFuncGetAttributes(&a, k);
+  if (e != hipSuccess) return e;
+  *regs = (a.numRegs + 7) & ~7;
+  *lds = (int)a.sharedSizeBytes;
+  return hipSuccess;
+}
+
+// (the grid beside a fetch kernel waits for each k-group in its K loop: ROW = false)
+template <int BM, int DT, bool LK>
+hipError_t fits_t(bool* fits) {
+  int fr = 0, fl = 0, r = 0, l = 0;
+  const void* fk = LK ? reinterpret_cast<const void*>(&agmm_fetch_k<BM>)
+                      : reinterpret_cast<const void*>(&agmm_fetch_m<BM>);
+  hipError_t e = footprint(fk, &fr, &fl);
+  if (e != hipSuccess) return e;
+  e = footprint(reinterpret_cast<const void*>(&agmm_persistent<BM, DT, true, LK, false>), &r, &l);
+  if (e != hipSuccess) return e;
+  // a SIMD holds 512 registers per lane; a CU 160 KiB of LDS
+  *fits = r + fr <= 512 && l + fl <= 160 * 1024;
+  return hipSuccess;
+}
+
+template <int BM>
+hipError_t fits_dt(int dtype, bool layout_k, bool* fits) {
+  if (dtype == AGMM_BF16)
+    return layout_k ? fits_t<BM, AGMM_BF16, true>(fits) : fits_t<BM, AGMM_BF16, false>(fits);
+  return layout_k ? fits_t<BM, AGMM_F16, true>(fits) : fits_t<BM, AGMM_F16, false>(fits);
+}
+}  // namespace
+
+hipError_t fetch_fits_beside(int dtype, int block_m, bool layout_k, bool* fits) {
+  switch (block_m) {
+    case 256: return fits_dt<256>(dtype, layout_k, fits);
+    case 128: return fits_dt<128>(dtype, layout_k, fits);
+    case 64: return fits_dt<64>(dtype, layout_k, fits);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_upload32(uint32_t* dst, const uint32_t* src, int64_t n, hipStream_t s) {

@@ -122,6 +122,15 @@ typedef struct agmm_desc {
   int32_t debug_fetch_delay;
   uint32_t debug_fetch_seed;
   int32_t debug_fetch_reverse;
+  /* Where the fused algorithm's fetchers run. 1: as a kernel of their own, launched on a
+   * stream of the handle's beside the persistent GEMM grid, which then has no fetchers: one
+   * fetch workgroup shares each CU with a GEMM workgroup, so every CU computes from the
+   * start (the caller's stream orders the fetch kernel after the work before the run and
+   * waits for it before the work after). UNSUPPORTED when a fetch workgroup does not fit
+   * on a CU beside a GEMM workgroup. -1: fetcher workgroups inside the persistent grid.
+   * 0 = auto: inside the grid. num_fetch_wgs then counts the fetch kernel's workgroups
+   * (0 = auto: one per CU, at most one per unit). */
+  int32_t fetch_kernel;
 } agmm_desc;
 
 /* Configuration resolved by create (read back with ag_matmul_get_config). */
@@ -151,6 +160,9 @@ typedef struct agmm_config {
   int32_t pipeline_chunks;      /* AGMM_ALGO_PIPELINED: chunks S actually used (0 otherwise) */
   int32_t pipeline_streams;     /* AGMM_ALGO_PIPELINED: streams the chunks rotate over, min(S, 4):
                                    the caller's, and pipeline_streams - 1 of the handle's */
+  int32_t fetch_kernel;         /* fused: 1 when the num_fetch_wgs fetchers run as a kernel of
+                                   their own beside the num_wgs GEMM workgroups; 0 when they are
+                                   workgroups of the persistent grid (num_wgs includes them) */
 } agmm_config;
 
 typedef struct agmm_handle agmm_handle;
@@ -226,7 +238,8 @@ int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* 
  * process ends; its address is looked up once per device); the caller still passes inputs
  * and outputs exactly as for ag_matmul_run, on the current device.
  *   desc: as for ag_matmul_create; algo FUSED or BASELINE; debug, gather_a, tail_split and
- *         the fetch stress knobs must be 0 (UNSUPPORTED otherwise). The workspace create would use for it,
+ *         the fetch stress knobs must be 0, and fetch_kernel must not be 1 (a fetch kernel
+ *         needs a stream of the handle's): UNSUPPORTED otherwise. The workspace create would use for it,
  *         ag_matmul_workspace_bytes(desc) on this device, must fit the scratch, else
  *         TOO_LARGE and nothing is enqueued: a staging buffer of up to 64 MiB, e.g.
  *         4096 x 8192 16-bit elements of A.

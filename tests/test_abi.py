@@ -77,6 +77,10 @@ def test_validation_errors(A):
     assert _ws(A, D=1, M=8, N=8, K=8, has_bias=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, tail_split=2) == INV
     assert _ws(A, D=1, M=8, N=8, K=8, gather_a=2) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, fetch_kernel=2) == INV
+    assert _ws(A, D=1, M=8, N=8, K=8, fetch_kernel=-2) == INV
+    assert _ws(A, D=2, M=16, N=8, K=8, fetch_kernel=1) > 0
+    assert _ws(A, D=2, M=16, N=8, K=8, fetch_kernel=-1) > 0
     # a queue entry holds the tile id in 24 bits: 4096 x 4096 tiles of 64 fit, 4097 x 4096 not
     assert _ws(A, D=1, M=(1 << 18) + 64, N=1 << 18, K=8, block_m=64) == UNS
     assert _ws(A, D=1, M=1 << 18, N=1 << 18, K=8, block_m=64) > 0

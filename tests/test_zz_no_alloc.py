@@ -80,6 +80,6 @@ def test_no_alloc_entry_point():
     assert rc == -8  # TOO_LARGE
     # refused options
     for kw in (dict(debug=1), dict(gather_a=1), dict(tail_split=1),
-               dict(algo=A.ALGO_PIPELINED)):
+               dict(algo=A.ALGO_PIPELINED), dict(fetch_kernel=1)):
         d = A.ag_matmul_desc_init(D=2, M=256, N=256, K=256, **kw)
         assert A.ag_matmul_run_static(d, [0, 0], 0, 0, 0, 0) == -2, kw
