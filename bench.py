@@ -324,6 +324,17 @@ def block_times(w, ops, dev, torch, blocks, per):
     return {n: statistics.median(v) for n, v in res.items()}
 
 
+def standalone_ops(w, A, tun):
+    """Handles timed in sustained blocks against each other: the fused run (fetchers in the
+    grid), the barrier baseline, and the fused run with its fetch as a kernel of its own
+    beside the grid (fetch_kernel=1; 'fetch_kernel')."""
+    mk = lambda algo, **kw: A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout,
+                                       algo=algo, rank=w.rank, direct_local=w.direct_local,
+                                       has_bias=w.has_bias, **{**tun, **kw})
+    return [("fused", mk("fused", fetch_kernel=-1)), ("baseline", mk("baseline")),
+            ("fetch_kernel", mk("fused", fetch_kernel=1))]
+
+
 def cold_times(op, dev, torch, reps, flush_bytes=1 << 30):
     """ms of single runs, each after 1 GiB of unrelated writes (untimed) have pushed the
     op's working set out of the caches."""
@@ -506,6 +517,8 @@ def main():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--fetch-wgs", type=int, default=0)
     ap.add_argument("--k-per-flag", type=int, default=0)
+    ap.add_argument("--fetch-kernel", action="store_true",
+                    help="fused: run the fetch as a kernel of its own beside the GEMM grid")
     ap.add_argument("--timeline", action="store_true",
                     help="only print the fused kernel's fetch/GEMM timeline from a debug trace "
                          "(for each of --workload, or of all five workloads with --sweep)")
@@ -555,6 +568,8 @@ def main():
         tun["num_fetch_wgs"] = args.fetch_wgs
     if args.k_per_flag:
         tun["k_per_flag"] = args.k_per_flag
+    if args.fetch_kernel:
+        tun["fetch_kernel"] = 1
 
     if args.sweep:
         rows = []
@@ -563,9 +578,7 @@ def main():
                                             args.warmup, torch, A, **tun)
             ym = yardstick_matmul(w, dev, args.steps, args.warmup, torch)
             mf, mb, mp = med["fused"], med["baseline"], med["pipelined"]
-            bops = [(a, A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=a,
-                                   rank=w.rank, direct_local=w.direct_local,
-                                   has_bias=w.has_bias, **tun)) for a in ("fused", "baseline")]
+            bops = standalone_ops(w, A, tun)
             bt = block_times(w, bops, dev, torch, 6, 10)
             for _, op in bops:
                 op.close()
@@ -575,6 +588,7 @@ def main():
                    "baseline_ms_median": mb, "speedup": mb / mf,
                    "fused_ms_standalone": bt["fused"], "baseline_ms_standalone": bt["baseline"],
                    "speedup_standalone": bt["baseline"] / bt["fused"],
+                   "fetch_kernel_ms_standalone": bt["fetch_kernel"],
                    "pipelined_ms_median": mp,
                    "pipelined_chunks": cfgs["pipelined"]["pipeline_chunks"],
                    "fused_tflops": tflops(w.M, w.N, w.K, mf / 1e3),
@@ -652,13 +666,12 @@ def main():
                                                           if other == "baseline" else
                                                           (med[args.algo] / mb), 3)}
         if args.algo == "fused":
-            bops = [(a, A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=a,
-                                   rank=w.rank, direct_local=w.direct_local,
-                                   has_bias=w.has_bias, **tun)) for a in ("fused", "baseline")]
+            bops = standalone_ops(w, A, tun)
             bt = block_times(w, bops, r["dev"], torch, 6, 10)
             res["standalone"] = {"fused_ms": round(bt["fused"], 5),
                                  "baseline_ms": round(bt["baseline"], 5),
                                  "fused_speedup": round(bt["baseline"] / bt["fused"], 3),
+                                 "fetch_kernel_ms": round(bt["fetch_kernel"], 5),
                                  "cold_fused_ms": round(cold_times(bops[0][1], r["dev"], torch, 10), 5),
                                  "cold_baseline_ms": round(cold_times(bops[1][1], r["dev"], torch, 10), 5)}
             res["clock"] = clock_under_load(bops[0][1], r["dev"], torch)
