@@ -141,3 +141,45 @@ def test_fetch_kernel_timeout_reported():
     assert A.ag_matmul_run(op.handle, ptrs, inp.B.data_ptr(), None, out.data_ptr(), s) == -7
     torch.cuda.synchronize()
     op.close()
+
+
+def test_fetch_kernel_on_a_side_stream_and_gather_only():
+    """Runs on a caller stream other than the default one: the fetch kernel is ordered after
+    the work before each run on that stream and the stream waits for it, so outputs of runs
+    alternating two input sets, read after synchronizing that stream alone, match the
+    baseline bit for bit. And a gathered-A handle with N = 0 (no output tile: the fetch
+    kernel alone writes the gathered A, beside a grid with nothing to compute)."""
+    import torch
+    import all_gather_gemm_amd as A
+    import oracle
+    w = Workload("fk_side", 4, 4 * 128, 264, 520, "f16", "normal_sqrtk", True, "m_contiguous",
+                 True, 780, rank=3)
+    sets = [make_inputs(w, seed=w.seed + i) for i in range(2)]
+    devs = [s.to("cuda") for s in sets]
+    refs = [out_bits(run_gpu(w, s, "baseline", dev_inp=d, block_m=64).out)
+            for s, d in zip(sets, devs)]
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
+                    block_m=64, k_per_flag=2, fetch_kernel=1)
+    side = torch.cuda.Stream()
+    outs = [torch.empty((w.M, w.N), dtype=torch.float16, device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for it in range(4):
+            i = it % 2
+            op.run(devs[i].shards, devs[i].B, devs[i].bias, out=outs[it])
+    side.synchronize()
+    for it in range(4):
+        assert np.array_equal(out_bits(outs[it]), refs[it % 2]), it
+    assert op.sync_status() == 0
+    op.close()
+
+    sh = [torch.randn(64, 72, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    A_ref = oracle.all_gather([bits(s.cpu()) for s in sh])
+    og = A.AgMatmul(2, 128, 0, 72, dtype="bf16", rank=1, gather_a=True, fetch_kernel=1)
+    assert og.config.fetch_kernel == 1
+    a_out = torch.full((128, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((72, 0), dtype=torch.bfloat16, device="cuda")
+    a, _ = og.run(sh, B, None, a_out=a_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(a).reshape(128, 72), A_ref)
+    og.close()
