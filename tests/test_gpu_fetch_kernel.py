@@ -26,6 +26,7 @@ CASES = [
     (3, 200, 328, 424, "f16", "m_contiguous", 256, 2, 0, 2),
     (8, 128, 1024, 1024, "bf16", "k_contiguous", 0, 0, 0, 3),
     (8, 512, 1024, 2048, "f16", "m_contiguous", 0, 0, 17, 5),
+    (2, 520, 520, 1032, "bf16", "k_contiguous", 256, 8, 0, 0),
 ]
 KNOBS = [dict(), dict(debug_fetch_reverse=1), dict(debug_fetch_delay=64, debug_fetch_seed=3)]
 
