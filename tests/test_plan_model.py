@@ -29,7 +29,8 @@ def problems(draw):
               num_fetch_wgs=draw(st.sampled_from([0, 0, 1, 5, 32, 300])),
               num_wgs=draw(st.sampled_from([0, 0, 7, 100, 300])),
               tail_split=int(draw(st.booleans())), gather_a=int(gather),
-              pipeline_chunks=draw(st.sampled_from([0, 1, 2, 3, 4, 8])))
+              pipeline_chunks=draw(st.sampled_from([0, 1, 2, 3, 4, 8])),
+              fetch_kernel=draw(st.sampled_from([0, 0, -1, 1])))
     return kw, draw(st.sampled_from([256, 80, 304]))
 
 
@@ -61,7 +62,15 @@ def test_planner_matches_model(prob):
     assert sorted(tiles) == list(range(g.T_m * g.T_n))
     for pieces in tiles.values():
         assert sorted(pieces) == list(range(len(pieces)))
-    if kw["algo"] == A.ALGO_FUSED and c.num_units:
+    fk = kw["algo"] == A.ALGO_FUSED and c.num_units > 0 and kw["fetch_kernel"] == 1
+    assert c.fetch_kernel == int(fk)
+    if fk:
+        # the fetch kernel's workgroups beside a grid of GEMM workgroups only
+        w_base = min(kw["num_wgs"] or cus, cus)
+        assert c.num_fetch_wgs == min(kw["num_fetch_wgs"] or cus, c.num_units)
+        assert c.num_wgs == max(1, min(w_base, c.num_items))
+        assert c.row_wait == 0
+    elif kw["algo"] == A.ALGO_FUSED and c.num_units:
         assert c.row_wait == int(c.num_fetch_wgs >= c.num_units)
         assert 1 <= c.num_fetch_wgs <= c.num_wgs
     if kw["algo"] == A.ALGO_PIPELINED:
