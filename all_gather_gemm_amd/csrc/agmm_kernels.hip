@@ -954,8 +954,6 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
 constexpr int kCopyBatch = 16;
 template <bool LAYOUT_K>
 constexpr int kSmallCopyBatch = LAYOUT_K ? 4 : 8;
-// VGPRs per lane the fetch kernel may use (its two instances' attributes): 512 minus the
-// GEMM waves' allocation, 424 with m_contiguous staging and 440 with k_contiguous.
 
 // Source row pointers of one unit: rows m_beg .. m_beg + R - 1 of the gathered A. A unit
 // inside one shard (the usual case) needs no per-row shard lookup.
@@ -1412,6 +1410,7 @@ __device__ __attribute__((always_inline)) void fetch_kernel_body(const KParams& 
     }
   }
 }
+// The VGPR cap of each instance is 512 minus the allocation of the GEMM waves it runs beside.
 // m_contiguous staging: beside GEMM waves of 424 registers
 template <int BM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_vgpr(88)))
