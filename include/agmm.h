@@ -185,7 +185,9 @@ void ag_matmul_desc_init(agmm_desc* desc);
  * Every handle also owns 16 bytes of pinned host memory (hipHostMalloc) into which its
  * kernels copy a flag-wait timeout (see ag_matmul_run).
  * AGMM_ALGO_PIPELINED handles also create their HIP streams (up to 3, default priority,
- * non-blocking) and events here.
+ * non-blocking) and events here; fused handles with fetch_kernel = 1 one stream (default
+ * priority, non-blocking) and two events, after checking that a fetch workgroup fits on a
+ * CU beside a GEMM workgroup (UNSUPPORTED otherwise).
  * Returns AGMM_OK and *out_handle, or INVALID_ARG (also: a misaligned or too small
  * workspace) / UNSUPPORTED / OOM / HIP.
  * Shape rules: M % D == 0; N % 8 == 0 and K % 8 == 0 (16-byte rows); m_contiguous also
@@ -205,6 +207,10 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * Every device pointer must be 16-byte aligned. The caller keeps all buffers alive until
  * the stream work completes. One run may be in flight per handle; successive runs on one
  * stream are safe; concurrent runs of one handle on different streams are undefined.
+ * With fetch_kernel = 1 the run records an event on hip_stream, makes the handle's stream
+ * wait for it, launches the fetch kernel there and the GEMM grid on hip_stream, then makes
+ * hip_stream wait for the handle's stream: work enqueued on hip_stream afterwards sees the
+ * whole run, as without the fetch kernel.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
  * or TIMEOUT. A flag wait that exceeds the spin limit makes every workgroup of the launch
  * stop early (the output is then incomplete); the launch's last workgroup copies the
