@@ -45,6 +45,9 @@ struct agmm_handle {
   std::vector<uint32_t> h_units, h_mtiles, h_qtiles;
   int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
   bool poisoned;
+  // ag_matmul_run_static: the run clears its flags and counters first and runs at epoch 1,
+  // so a captured graph of it stays valid on every replay
+  bool clears_flags;
   // AGMM_ALGO_PIPELINED
   std::vector<PipeChunk> chunks;
   uint32_t *c_units, *c_mtiles, *c_qtiles, *c_ctr;
@@ -486,6 +489,15 @@ bool timed_out(agmm_handle* h) {
   return true;
 }
 
+// A run whose kernels compare flags or split counters with the handle's epoch fixes that
+// epoch when it is enqueued; a captured graph would replay it with the same epoch and the
+// waits would no longer order anything. Such runs refuse a stream that is capturing.
+int refuse_capture(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  AGMM_HIP(hipStreamIsCapturing(s, &cs));
+  return cs == hipStreamCaptureStatusNone ? AGMM_OK : AGMM_ERR_UNSUPPORTED;
+}
+
 // Destroys the pipeline's streams and events created so far (errors ignored: teardown).
 void release_streams(agmm_handle* h) {
   for (int j = 0; j < h->n_pstreams; ++j) (void)hipStreamDestroy(h->pstreams[j]);
@@ -849,6 +861,10 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   if (c.num_tiles == 0 && c.num_units == 0) return AGMM_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  if ((d.algo == AGMM_ALGO_FUSED || c.split_tiles > 0) && !h->clears_flags) {
+    const int rc = refuse_capture(s);
+    if (rc != AGMM_OK) return rc;
+  }
   if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
     AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
     AGMM_HIP(agmm::launch_fill32(h->split_cnt, c.split_tiles, 0u, s));
@@ -1094,6 +1110,10 @@ int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void*
   }
   if (c.num_tiles == 0) return AGMM_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  {
+    const int rc = refuse_capture(s);
+    if (rc != AGMM_OK) return rc;
+  }
   if (h->ar_epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
     AGMM_HIP(agmm::launch_fill32(h->ar_flags, h->ar_flags_n, 0u, s));
     h->ar_epoch = 0;
@@ -1249,6 +1269,9 @@ struct StaticTables {
   bool valid;
   agmm_desc desc;
   int num_cus;
+  // A run was captured on this device: its graph rewrites the tables whenever it replays, so
+  // from then on every run uploads its own tables instead of trusting the cache.
+  bool captured;
 };
 std::mutex g_static_mu;
 StaticTables g_static_tables[64];
@@ -1287,16 +1310,20 @@ int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const
   h.ws = static_cast<char*>(base);
   h.own_ws = false;
   h.host_status = nullptr;
+  h.clears_flags = true;
   carve_workspace(&h, pl);
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   // Flags, counters and split counters start at zero: one fill kernel (not a memset, which
   // a captured graph would record as a memset node). The run is then epoch 1.
   AGMM_HIP(agmm::launch_fill32(reinterpret_cast<uint32_t*>(h.ws + pl.off_flags),
                                (pl.off_units - pl.off_flags) / 4, 0u, s));
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  AGMM_HIP(hipStreamIsCapturing(s, &cs));
   {
     std::lock_guard<std::mutex> lock(g_static_mu);
     StaticTables& t = g_static_tables[dev];
-    if (!(t.valid && t.num_cus == num_cus && same_desc(t.desc, *desc))) {
+    if (cs != hipStreamCaptureStatusNone) t.captured = true;
+    if (t.captured || !(t.valid && t.num_cus == num_cus && same_desc(t.desc, *desc))) {
       t.valid = false;
       AGMM_HIP(agmm::launch_upload32(h.units, pl.units.data(), (int64_t)pl.units.size(), s));
       AGMM_HIP(agmm::launch_upload32(h.mtiles, pl.mtiles.data(), (int64_t)pl.mtiles.size(), s));

@@ -211,8 +211,13 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * wait for it, launches the fetch kernel there and the GEMM grid on hip_stream, then makes
  * hip_stream wait for the handle's stream: work enqueued on hip_stream afterwards sees the
  * whole run, as without the fetch kernel.
+ * Graph capture: a FUSED run, and a run with split tiles (tail_split), compares flags and
+ * counters with the handle's run number, which is fixed when the run is enqueued; a
+ * captured graph would replay it with a number the flags already hold. Such a run on a
+ * capturing stream returns UNSUPPORTED and enqueues nothing; ag_matmul_run_static is the
+ * entry point for capture. A BASELINE run without split tiles may be captured.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
- * or TIMEOUT. A flag wait that exceeds the spin limit makes every workgroup of the launch
+ * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes every workgroup of the launch
  * stop early (the output is then incomplete); the launch's last workgroup copies the
  * status words into the handle's pinned host word. In debug mode run() synchronizes and
  * returns TIMEOUT for that run itself. Otherwise run() does not synchronize: the first
@@ -231,7 +236,7 @@ int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, cons
  *               buffer; row m = row m - d*M/D of shard d. It is the run's staging buffer:
  *               its contents are undefined until the stream work completes.
  * Returns AGMM_OK, or INVALID_ARG (also for a handle without gather_a), WRONG_DEVICE,
- * POISONED, HIP, or (debug) TIMEOUT.
+ * POISONED, HIP, UNSUPPORTED (graph capture, as for ag_matmul_run) or (debug) TIMEOUT.
  */
 int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* B,
                          const void* bias, void* out, void* a_gathered, void* hip_stream);
@@ -251,8 +256,10 @@ int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* 
  *         4096 x 8192 16-bit elements of A.
  * Enqueues on `hip_stream`: a fill kernel that clears the scratch's flags and counters,
  * kernels that write the schedule tables (skipped when this device's previous call had the
- * same desc), then the run's kernels. Nothing is synchronized, and no host memory has to
- * outlive the call. Every call on one device shares that device's scratch: calls whose
+ * same desc, unless a call on this device has ever been captured), then the run's kernels.
+ * Nothing is synchronized, and no host memory has to outlive the call. Every call starts
+ * from cleared flags, so it may be captured into a HIP graph and the graph replayed any
+ * number of times; each replay rewrites the tables it uses. Every call on one device shares that device's scratch: calls whose
  * stream work overlaps (other streams, other host threads) race on it and their outputs
  * are undefined; calls on one stream are ordered and safe. A flag-wait timeout (a fetch
  * unit never published, which normal runs do not produce) ends the launch early with an
@@ -304,7 +311,8 @@ int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* 
  * ag_gemm_ar_flags_run: enqueues the op on `hip_stream`. A_parts[r]: device [M, K_local]
  *   row-major; B_parts[r]: device [K_local, N] row-major (r < D); bias [N] 16-bit or NULL;
  *   out [M, N] 16-bit row-major, not overlapping any input. All 16-byte aligned. Runs of
- *   one handle on several streams at once race on its partial buffer and flags.
+ *   one handle on several streams at once race on its partial buffer and flags. Its flags
+ *   are compared with the handle's run number, so a capturing stream gets UNSUPPORTED.
  * Return codes as for ag_matmul_run. */
 int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dtype,
                             int block_m, agmm_handle** out_handle);
