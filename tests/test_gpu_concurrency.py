@@ -2,11 +2,11 @@
 
 Each handle owns its workspace (staging, flags, counters, queues), so runs of different
 handles on different streams, enqueued so that they can overlap, do not interfere. When the
-persistent grids of two handles share the chip, each grid's fetcher workgroups are its lowest-numbered ones and
-are dispatched first, so every flag wait of either grid ends. Runs of each handle alternate
-between two input sets on its stream, with the other stream's runs enqueued between them.
-Every output must match the same handle's eager run on the same inputs bit for bit, and one
-of each handle's outputs must be within the oracle's tolerance.
+persistent grids of two handles share the chip, each grid's fetcher workgroups are its
+lowest-numbered ones and are dispatched first, so every flag wait of either grid ends. Runs
+of each handle alternate between two input sets on its stream, with the other stream's runs
+enqueued between them. Every output must match the same handle's eager run on the same
+inputs bit for bit, and one of each handle's outputs must be within the oracle's tolerance.
 """
 import numpy as np
 import pytest
