@@ -861,7 +861,8 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   if (c.num_tiles == 0 && c.num_units == 0) return AGMM_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  if ((d.algo == AGMM_ALGO_FUSED || c.split_tiles > 0) && !h->clears_flags) {
+  // (a debug run also synchronizes the stream, which a capturing stream does not allow)
+  if ((d.algo == AGMM_ALGO_FUSED || c.split_tiles > 0 || d.debug) && !h->clears_flags) {
     const int rc = refuse_capture(s);
     if (rc != AGMM_OK) return rc;
   }

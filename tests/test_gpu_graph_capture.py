@@ -9,7 +9,8 @@ fused and baseline algorithms and both staging layouts.
 The runs whose kernels compare flags or split counters with a handle's run number (a fused
 handle, a handle with split tiles, the per-tile flag all-reduce) fix that number when they
 are enqueued, so they refuse a capturing stream with UNSUPPORTED and enqueue nothing; the
-handle then runs eagerly as before. A baseline handle without split tiles compares nothing
+handle then runs eagerly as before. A debug run, which synchronizes its stream, refuses it
+too. A baseline handle without split tiles compares nothing
 with a run number and may be captured and replayed.
 """
 import ctypes
@@ -135,6 +136,9 @@ def test_epoch_runs_refuse_capture():
                             block_m=64, algo="baseline", tail_split=1),
         "fetch_kernel": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank,
                                    has_bias=True, block_m=64, fetch_kernel=1),
+        # a debug run synchronizes its stream
+        "debug": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
+                            block_m=64, algo="baseline", debug=True),
     }
     assert handles["split"].config.split_tiles > 0
     out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
