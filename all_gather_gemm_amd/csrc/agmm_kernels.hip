@@ -941,12 +941,15 @@ __device__ inline void load_shard_table(const KParams& p, const uint16_t** table
   __syncthreads();
 }
 
-// A fetcher workgroup's copy rate is bound by latency, not by its share of the HBM
-// bandwidth, so the copies run as a two-batch software pipeline: the loads of batch n + 1
-// are issued before the stores of batch n, so neither waits for the other (a wait for
-// loads also waits for every store issued before them: the vector memory counter retires
-// in order). A batch is BATCH 16-byte loads per thread (kCopyBatch: 64 KiB per workgroup);
-// at most three batches of requests are in flight, within the counter's range of 63. The
+// A fetcher workgroup copies far below its share of the HBM bandwidth, so the copies run as
+// a two-batch software pipeline: the loads of batch n + 1 are issued before the stores of
+// batch n, so neither waits for the other (a wait for loads also waits for every store
+// issued before them: the vector memory counter retires in order). A batch is BATCH
+// 16-byte loads per thread (kCopyBatch: 64 KiB per workgroup); at most three batches of
+// requests are in flight, within the counter's range of 63. More requests in flight do not
+// make the fused run faster: with 24 loads per batch the fetchers finish sooner, but their
+// denser traffic slows the GEMM workgroups beside them by more (8 per batch ran as fast as
+// 16). The
 // fetch kernel that runs beside the GEMM kernel takes kSmallCopyBatch, so that its data
 // registers (two batches) fit in what a GEMM wave leaves of a SIMD's register file
 // (8 for the m_contiguous copy, whole 8x8 blocks; 4 for the k_contiguous one, whose GEMM
