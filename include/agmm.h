@@ -215,12 +215,12 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * counters with the handle's run number, which is fixed when the run is enqueued; a
  * captured graph would replay it with a number the flags already hold. Such a run on a
  * capturing stream returns UNSUPPORTED and enqueues nothing; ag_matmul_run_static is the
- * entry point for capture. So does a debug run, which synchronizes the stream. A BASELINE
- * run without split tiles or debug may be captured.
+ * entry point for capture. A debug run, which synchronizes the stream, is refused the same
+ * way. A BASELINE run without split tiles or debug may be captured.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
- * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes every workgroup of the launch
- * stop early (the output is then incomplete); the launch's last workgroup copies the
- * status words into the handle's pinned host word. In debug mode run() synchronizes and
+ * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes
+ * every workgroup of the launch stop early (the output is then incomplete); the launch's
+ * last workgroup copies the status words into the handle's pinned host word. In debug mode run() synchronizes and
  * returns TIMEOUT for that run itself. Otherwise run() does not synchronize: the first
  * later call on the handle (run, or ag_matmul_sync_status, which waits for the device)
  * that finds the word set returns TIMEOUT and poisons the handle; calls after that return
