@@ -219,12 +219,12 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * way. A BASELINE run without split tiles or debug may be captured.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
  * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes
- * every workgroup of the launch stop early (the output is then incomplete); the launch's
- * last workgroup copies the status words into the handle's pinned host word. In debug mode run() synchronizes and
- * returns TIMEOUT for that run itself. Otherwise run() does not synchronize: the first
- * later call on the handle (run, or ag_matmul_sync_status, which waits for the device)
- * that finds the word set returns TIMEOUT and poisons the handle; calls after that return
- * POISONED. The same holds for the GEMM + all-reduce entry points.
+ * every workgroup of the launch stop early (the output is then incomplete); the launch's last
+ * workgroup copies the status words into the handle's pinned host word. In debug mode run()
+ * synchronizes and returns TIMEOUT for that run itself. Otherwise run() does not synchronize:
+ * the first later call on the handle (run, or ag_matmul_sync_status, which waits for the
+ * device) that finds the word set returns TIMEOUT and poisons the handle; calls after that
+ * return POISONED. The same holds for the GEMM + all-reduce entry points.
  */
 int ag_matmul_run(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
                   void* out, void* hip_stream);
@@ -251,20 +251,20 @@ int ag_matmul_run_gather(agmm_handle* h, const void* const* shards, const void* 
  * and outputs exactly as for ag_matmul_run, on the current device.
  *   desc: as for ag_matmul_create; algo FUSED or BASELINE; debug, gather_a, tail_split and
  *         the fetch stress knobs must be 0, and fetch_kernel must not be 1 (a fetch kernel
- *         needs a stream of the handle's): UNSUPPORTED otherwise. The workspace create would use for it,
- *         ag_matmul_workspace_bytes(desc) on this device, must fit the scratch, else
- *         TOO_LARGE and nothing is enqueued: a staging buffer of up to 64 MiB, e.g.
- *         4096 x 8192 16-bit elements of A.
+ *         needs a stream of the handle's): UNSUPPORTED otherwise. The workspace create
+ *         would use for it, ag_matmul_workspace_bytes(desc) on this device, must fit the
+ *         scratch, else TOO_LARGE and nothing is enqueued: a staging buffer of up to
+ *         64 MiB, e.g. 4096 x 8192 16-bit elements of A.
  * Enqueues on `hip_stream`: a fill kernel that clears the scratch's flags and counters,
  * kernels that write the schedule tables (skipped when this device's previous call had the
  * same desc, unless a call on this device has ever been captured), then the run's kernels.
- * Nothing is synchronized, and no host memory has to outlive the call. Every call starts
- * from cleared flags, so it may be captured into a HIP graph and the graph replayed any
- * number of times; each replay rewrites the tables it uses. Every call on one device shares that device's scratch: calls whose
- * stream work overlaps (other streams, other host threads) race on it and their outputs
- * are undefined; calls on one stream are ordered and safe. A flag-wait timeout (a fetch
- * unit never published, which normal runs do not produce) ends the launch early with an
- * incomplete output and is not reported by this entry point.
+ * Nothing is synchronized, and no host memory has to outlive the call. Every call starts from
+ * cleared flags, so it may be captured into a HIP graph and the graph replayed any number of
+ * times; each replay rewrites the tables it uses. Every call on one device shares that
+ * device's scratch: calls whose stream work overlaps (other streams, other host threads) race
+ * on it and their outputs are undefined; calls on one stream are ordered and safe. A flag-wait
+ * timeout (a fetch unit never published, which normal runs do not produce) ends the launch
+ * early with an incomplete output and is not reported by this entry point.
  * Returns AGMM_OK, INVALID_ARG, UNSUPPORTED, TOO_LARGE, WRONG_DEVICE or HIP.
  */
 int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const void* B,
@@ -379,7 +379,8 @@ int ag_matmul_sync_status(agmm_handle* h);
  * of wave 0, after the per-workgroup event ids of the iris issue (wg_fetch, wg_gemm,
  * wg_gemm_wait). Timestamps are the GPU's constant 100 MHz real-time counter. */
 #define AGMM_EV_FETCH 1      /* id = unit index, a = m-tile, b = k-group */
-#define AGMM_EV_GEMM 2       /* id = queue entry (tile id and piece, as in AGMM_Q_QUEUES), a = m-tile, b = n-tile */
+#define AGMM_EV_GEMM 2       /* id = queue entry (tile id and piece, as in AGMM_Q_QUEUES),
+                                a = m-tile, b = n-tile */
 #define AGMM_EV_GEMM_WAIT 3  /* id = flag index, a = value seen, b = polls */
 
 typedef struct agmm_trace_rec {
