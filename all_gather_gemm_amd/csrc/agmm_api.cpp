@@ -45,9 +45,6 @@ struct agmm_handle {
   std::vector<uint32_t> h_units, h_mtiles, h_qtiles;
   int32_t qoff[agmm::kQueueSlots], qlen[agmm::kQueueSlots];
   bool poisoned;
-  // ag_matmul_run_static: the run clears its flags and counters first and runs at epoch 1,
-  // so a captured graph of it stays valid on every replay
-  bool clears_flags;
   // AGMM_ALGO_PIPELINED
   std::vector<PipeChunk> chunks;
   uint32_t *c_units, *c_mtiles, *c_qtiles, *c_ctr;
@@ -69,7 +66,6 @@ struct agmm_handle {
   uint32_t* ar_flags;
   uint32_t* ar_items;
   int64_t ar_flags_n, ar_items_n;
-  uint32_t ar_epoch;
 };
 
 namespace {
@@ -489,9 +485,10 @@ bool timed_out(agmm_handle* h) {
   return true;
 }
 
-// A run whose kernels compare flags or split counters with the handle's epoch fixes that
-// epoch when it is enqueued; a captured graph would replay it with the same epoch and the
-// waits would no longer order anything. Such runs refuse a stream that is capturing.
+// Runs that a captured graph could not replay refuse a capturing stream: a debug run
+// synchronizes the stream, and a fetch-kernel run orders a second stream of the handle's
+// with events. (The kernels count runs on the device, so a fused run itself replays
+// correctly.)
 int refuse_capture(hipStream_t s) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   AGMM_HIP(hipStreamIsCapturing(s, &cs));
@@ -740,7 +737,7 @@ namespace {
 
 // The launch parameters of a handle's run: its tables and counters, the given buffers.
 KParams run_params(agmm_handle* h, const void* const* shards, const void* B, const void* bias,
-                   void* out, uint16_t* staging, uint32_t epoch) {
+                   void* out, uint16_t* staging) {
   const agmm_desc& d = h->desc;
   const agmm_config& c = h->cfg;
   KParams p;
@@ -776,7 +773,6 @@ KParams run_params(agmm_handle* h, const void* const* shards, const void* B, con
   p.kpf = c.k_per_flag;
   p.num_units = c.num_units;
   p.num_tiles = c.num_tiles;
-  p.epoch = epoch;
   p.debug = d.debug;
   p.trace_cap = c.trace_cap;
   p.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpinLimit;
@@ -861,20 +857,14 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
   if (c.num_tiles == 0 && c.num_units == 0) return AGMM_OK;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  // (a debug run also synchronizes the stream, which a capturing stream does not allow)
-  if ((d.algo == AGMM_ALGO_FUSED || c.split_tiles > 0 || d.debug) && !h->clears_flags) {
+  if (c.fetch_kernel || d.debug) {
     const int rc = refuse_capture(s);
     if (rc != AGMM_OK) return rc;
   }
-  if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
-    AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
-    AGMM_HIP(agmm::launch_fill32(h->split_cnt, c.split_tiles, 0u, s));
-    h->cfg.epoch = 0;
-  }
-  const uint32_t epoch = ++h->cfg.epoch;
+  ++h->cfg.epoch;  // runs enqueued through the handle (the kernels count their own)
 
   KParams p = run_params(h, shards, B, bias, out,
-                          d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging, epoch);
+                          d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging);
 
   if (d.algo == AGMM_ALGO_FUSED && c.fetch_kernel) {
     // The fetch kernel on the handle's stream, after the caller's stream reaches this point;
@@ -1013,14 +1003,9 @@ int ag_gemm_ar_run(agmm_handle* h, const void* A_local, const void* B_local, flo
   }
   if (c.num_tiles == 0) return AGMM_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  if (h->cfg.epoch == UINT32_MAX) {  // epoch wrap, as in run_impl
-    AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, 0u, s));
-    AGMM_HIP(agmm::launch_fill32(h->split_cnt, c.split_tiles, 0u, s));
-    h->cfg.epoch = 0;
-  }
-  const uint32_t epoch = ++h->cfg.epoch;
+  ++h->cfg.epoch;
   const void* shards[1] = {A_local};
-  KParams p = run_params(h, shards, B_local, nullptr, nullptr, h->staging, epoch);
+  KParams p = run_params(h, shards, B_local, nullptr, nullptr, h->staging);
   p.F = 0;
   p.staged_kmajor = 1;
   p.debug = 0;
@@ -1111,16 +1096,8 @@ int ag_gemm_ar_flags_run(agmm_handle* h, const void* const* A_parts, const void*
   }
   if (c.num_tiles == 0) return AGMM_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  {
-    const int rc = refuse_capture(s);
-    if (rc != AGMM_OK) return rc;
-  }
-  if (h->ar_epoch == UINT32_MAX) {  // epoch wrap: clear the flags, restart at 1
-    AGMM_HIP(agmm::launch_fill32(h->ar_flags, h->ar_flags_n, 0u, s));
-    h->ar_epoch = 0;
-  }
-  const uint32_t epoch = ++h->ar_epoch;
-  KParams p = run_params(h, A_parts, nullptr, bias, out, h->staging, epoch);
+  ++h->cfg.epoch;
+  KParams p = run_params(h, A_parts, nullptr, bias, out, h->staging);
   for (int r = 0; r < D; ++r) {
     p.shards[r] = static_cast<const uint16_t*>(A_parts[r]);
     p.ar_B[r] = static_cast<const uint16_t*>(B_parts[r]);
@@ -1311,11 +1288,11 @@ int ag_matmul_run_static(const agmm_desc* desc, const void* const* shards, const
   h.ws = static_cast<char*>(base);
   h.own_ws = false;
   h.host_status = nullptr;
-  h.clears_flags = true;
   carve_workspace(&h, pl);
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  // Flags, counters and split counters start at zero: one fill kernel (not a memset, which
-  // a captured graph would record as a memset node). The run is then epoch 1.
+  // Flags, counters (the run counter too) and split counters start at zero: one fill kernel
+  // (not a memset, which a captured graph would record as a memset node). The run is then
+  // epoch 1.
   AGMM_HIP(agmm::launch_fill32(reinterpret_cast<uint32_t*>(h.ws + pl.off_flags),
                                (pl.off_units - pl.off_flags) / 4, 0u, s));
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

@@ -31,6 +31,8 @@ constexpr int kMaxSplit = 4;
 // Counter words in the workspace (uint32). Each queue counter has its own 128-byte line.
 enum : int {
   CTR_DONE = 0,         // workgroups that finished; the last one resets the queue counters
+  CTR_RUNS = 1,         // runs the workspace has finished (mod 2^32): the last workgroup of
+                        // run e stores e, so the next run's kernels read their epoch here
   CTR_STATUS = 2,       // 0 = ok, 1 = a flag wait timed out (sticky until the host clears it)
   CTR_STATUS_WG = 3,    // workgroup that timed out
   CTR_STATUS_FLAG = 4,  // flag index it waited on
@@ -70,7 +72,7 @@ struct KParams {
   int32_t num_units, num_tiles, F;
   int32_t staged_kmajor;    // 1: staging is [M][K]; 0: staging is [K][M]
   int32_t row_wait;         // fused: tiles wait at their start for all of their k-groups
-  uint32_t epoch;
+  uint32_t reserved;        // (unused: a run's epoch comes from ctr[CTR_RUNS] on the device)
   int32_t debug, trace_cap;
   uint32_t spin_limit;
   int32_t skip_unit;

@@ -18,7 +18,11 @@
 // barrier per K-tile; the output tile goes through LDS for 16-byte coalesced stores.
 //
 // Flag protocol: fetcher workgroups claim units from one counter; a unit's flag holds the
-// run's epoch once the unit is in staging. Producer = every wave waits until its stores
+// run's epoch once the unit is in staging. The epoch is counted on the device: run e reads
+// e - 1 from the workspace's run counter at its start and its last workgroup stores e, so
+// runs count up in stream order however they were enqueued (also as replays of a captured
+// graph). Flags and split counters grow by a fixed amount per run, and every comparison
+// with the epoch is an equality, so the uint32 counts may wrap. Producer = every wave waits until its stores
 // are acknowledged (they then sit in this XCD's L2: the vector L1 writes through),
 // workgroup barrier, then one agent-scope release add of 1 by thread 0, whose L2 write-back
 // publishes the whole workgroup's stores. Consumer =
@@ -289,6 +293,18 @@ __device__ inline void mirror_status(const KParams& p) {
   __hip_atomic_store(h, st, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Thread 0's first claim of a workgroup: the next queue entry into *next, and this run's
+// epoch into *epoch, one more than the runs the workspace has finished. The two loads are in
+// flight together. The run's last workgroup stores the epoch only after every workgroup has
+// counted itself done, so every workgroup reads the previous run's count.
+__device__ inline int grab(const KParams& p);
+__device__ inline void first_claim(const KParams& p, int* next, uint32_t* epoch) {
+  const uint32_t done = __hip_atomic_load(p.ctr + CTR_RUNS, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  *next = grab(p);
+  *epoch = done + 1u;
+}
+
 // Waits (every lane of the calling wave) until flags[idx] == target. No acquire: the caller
 // issues one for every flag it has seen complete.
 __device__ inline void poll_flag(const KParams& p, int64_t idx, uint32_t target, Tracer& tr) {
@@ -429,7 +445,8 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
                                                          int piece, int pieces, bool staged,
                                                          const Stages<T>& st, u32x2* bias_lds,
                                                          int tid_in, Tracer& tr, int* next_tile,
-                                                         int* is_last, int src = 0) {
+                                                         int* is_last, uint32_t epoch,
+                                                         int src = 0) {
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
   // this piece's K-tiles [kt_lo, kt_lo + KT)
   const int KT_all = (int)((p.K + BK - 1) / BK);
@@ -438,7 +455,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
   const int64_t fbase = (int64_t)t_m * p.G;
   bool waits = WAIT && staged;
   const int kpf = p.kpf;
-  const uint32_t target = p.epoch;  // a published unit's flag
+  const uint32_t target = epoch;  // a published unit's flag
   // Consumer side of the flags. An agent-scope acquire invalidates the XCD's L2 (which all
   // workgroups on that XCD rely on for operand reuse) and drains the wave's DMA requests in
   // flight, so acquires are few: only wave 0 polls and acquires, and each acquire also
@@ -725,7 +742,7 @@ __device__ __attribute__((always_inline)) void gemm_tile(const KParams& p, int t
     if (tid == 0) {
       const uint32_t done = __hip_atomic_fetch_add(p.split_cnt + sidx, 1u, __ATOMIC_RELEASE,
                                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
-      const bool last = done == (uint32_t)pieces * p.epoch;  // counters grow by `pieces` per run
+      const bool last = done == (uint32_t)pieces * epoch;  // counters grow by `pieces` per run
       if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       *is_last = last;
     }
@@ -1212,6 +1229,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
   __shared__ u32x2 s_bias[T::BN / 4];
   const Stages<T> st{(lds_u32x4*)lds_stages, (uint32_t)(size_t)(lds_void*)lds_stages};
   __shared__ int s_next, s_last, s_claim;
+  __shared__ uint32_t s_epoch;
   __shared__ const uint16_t* s_shards[AGMM_MAX_SHARDS];
   const int tid = threadIdx.x, wg = blockIdx.x;
   Tracer tr{p.debug ? p.trace + (size_t)wg * p.trace_cap : nullptr, 0u, (uint32_t)p.trace_cap,
@@ -1228,10 +1246,10 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     }
   }
 
-
-  if (tid == 0) s_next = grab(p);
+  if (tid == 0) first_claim(p, &s_next, &s_epoch);
   __syncthreads();
   int q = __builtin_amdgcn_readfirstlane(s_next);  // uniform: tile addressing in SGPRs
+  const uint32_t epoch = uniform32(s_epoch);
   while (q >= 0) {
     __syncthreads();  // everyone has read s_next
     const int tile = (int)((uint32_t)q & kItemTileMask);
@@ -1242,14 +1260,14 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
     const bool staged = (e >> 31) == 0u;
     const uint64_t t0 = tr.now();
     if constexpr (!FUSED) {
-      gemm_tile<T, DT, true, false, false, EPI>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, false, false, EPI>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, epoch);
     } else if constexpr (LAYOUT_K) {
-      gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+      gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, epoch);
     } else {
       if (!staged)
-        gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, true, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, epoch);
       else
-        gemm_tile<T, DT, false, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last);
+        gemm_tile<T, DT, false, true, ROW>(p, t_m, t_n, piece, pieces, staged, st, s_bias, tid, tr, &s_next, &s_last, epoch);
     }
     tr.rec(AGMM_EV_GEMM, (uint32_t)q, (uint32_t)t_m, (uint32_t)t_n, t0);
     __syncthreads();
@@ -1267,6 +1285,7 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
       // beside it resets its own, and may still be claiming units nobody waits for)
       if (p.F > 0)
         __hip_atomic_store(p.ctr + CTR_FETCH, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctr + CTR_RUNS, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       mirror_status(p);
     }
@@ -1283,11 +1302,12 @@ __global__ __launch_bounds__(kThreads) void agmm_persistent(KParams p) {
 
 template <class T, int DT>
 __device__ __attribute__((always_inline)) void reduce_tile(const KParams& p, int t_m, int t_n,
-                                                           int tile, int tid, Tracer& tr) {
+                                                           int tile, int tid, Tracer& tr,
+                                                           uint32_t epoch) {
   constexpr int BM = T::BM, BN = T::BN;
   const int64_t tiles = (int64_t)p.T_m * p.T_n;
   if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
-    for (int r = 0; r < p.ar_D; ++r) poll_flag(p, r * tiles + tile, p.epoch, tr);
+    for (int r = 0; r < p.ar_D; ++r) poll_flag(p, r * tiles + tile, epoch, tr);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
@@ -1328,12 +1348,14 @@ __global__ __launch_bounds__(kThreads) void agmm_ar_flags(KParams p) {
   __shared__ u32x2 s_bias[T::BN / 4];
   const Stages<T> st{(lds_u32x4*)lds_stages, (uint32_t)(size_t)(lds_void*)lds_stages};
   __shared__ int s_next, s_last;
+  __shared__ uint32_t s_epoch;
   const int tid = threadIdx.x;
   Tracer tr{nullptr, 0u, 0u, false};
   const int64_t tiles = (int64_t)p.T_m * p.T_n;
-  if (tid == 0) s_next = grab(p);
+  if (tid == 0) first_claim(p, &s_next, &s_epoch);
   __syncthreads();
   int q = __builtin_amdgcn_readfirstlane(s_next);
+  const uint32_t epoch = uniform32(s_epoch);
   while (q >= 0) {
     __syncthreads();  // everyone has read s_next
     const int tile = (int)((uint32_t)q & kItemTileMask);
@@ -1341,14 +1363,14 @@ __global__ __launch_bounds__(kThreads) void agmm_ar_flags(KParams p) {
     if (((uint32_t)q & kArReduceItem) == 0u) {
       const int r = (int)(((uint32_t)q >> 24) & 63u);
       gemm_tile<T, DT, true, false, false, 2>(p, t_m, t_n, 0, 1, false, st, s_bias, tid, tr,
-                                              &s_next, &s_last, r);
+                                              &s_next, &s_last, epoch, r);
       wait_vmcnt<0>();  // this thread's stores of the partial tile are done
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(p.flags + r * tiles + tile, p.epoch, __ATOMIC_RELEASE,
+        __hip_atomic_store(p.flags + r * tiles + tile, epoch, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      reduce_tile<T, DT>(p, t_m, t_n, tile, tid, tr);
+      reduce_tile<T, DT>(p, t_m, t_n, tile, tid, tr, epoch);
       if (tid == 0) s_next = grab(p);
     }
     __syncthreads();
@@ -1360,6 +1382,7 @@ __global__ __launch_bounds__(kThreads) void agmm_ar_flags(KParams p) {
       for (int x = 0; x < kQueueSlots; ++x)
         __hip_atomic_store(p.ctr + CTR_Q + x * CTR_QSTRIDE, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctr + CTR_RUNS, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(p.ctr + CTR_DONE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       mirror_status(p);
     }

@@ -144,7 +144,9 @@ typedef struct agmm_config {
   int32_t num_wgs;              /* W, fused grid (fetchers included) */
   int32_t num_copy_wgs;         /* baseline copy-kernel grid */
   int32_t trace_cap;
-  uint32_t epoch;               /* epoch of the last run (0 before the first) */
+  uint32_t epoch;               /* runs enqueued through the handle's run entry points (0
+                                   before the first); a replay of a captured graph is not
+                                   counted here. The kernels count runs on the device. */
   int64_t staging_elems;        /* 16-bit elements in the handle's staging buffer (0 with
                                    gather_a: the caller's buffer is the staging) */
   int64_t workspace_bytes;      /* device bytes the handle owns */
@@ -211,12 +213,13 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * wait for it, launches the fetch kernel there and the GEMM grid on hip_stream, then makes
  * hip_stream wait for the handle's stream: work enqueued on hip_stream afterwards sees the
  * whole run, as without the fetch kernel.
- * Graph capture: a FUSED run, and a run with split tiles (tail_split), compares flags and
- * counters with the handle's run number, which is fixed when the run is enqueued; a
- * captured graph would replay it with a number the flags already hold. Such a run on a
- * capturing stream returns UNSUPPORTED and enqueues nothing; ag_matmul_run_static is the
- * entry point for capture. A debug run, which synchronizes the stream, is refused the same
- * way. A BASELINE run without split tiles or debug may be captured.
+ * Graph capture: the run's kernels take its epoch (the value its flags and split counters
+ * must reach) from a run counter in the workspace, which the last workgroup of every run
+ * advances. A run may therefore be captured into a HIP graph, and the graph replayed any
+ * number of times, interleaved with eager runs of the same handle on the same stream. Two
+ * kinds of run return UNSUPPORTED on a capturing stream and enqueue nothing: a debug run,
+ * which synchronizes the stream, and a fetch_kernel = 1 run, which orders a stream of the
+ * handle's with events.
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
  * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes
  * every workgroup of the launch stop early (the output is then incomplete); the launch's last
@@ -312,8 +315,8 @@ int ag_gemm_ar_finalize(agmm_handle* h, const float* C, const void* bias, void* 
  * ag_gemm_ar_flags_run: enqueues the op on `hip_stream`. A_parts[r]: device [M, K_local]
  *   row-major; B_parts[r]: device [K_local, N] row-major (r < D); bias [N] 16-bit or NULL;
  *   out [M, N] 16-bit row-major, not overlapping any input. All 16-byte aligned. Runs of
- *   one handle on several streams at once race on its partial buffer and flags. Its flags
- *   are compared with the handle's run number, so a capturing stream gets UNSUPPORTED.
+ *   one handle on several streams at once race on its partial buffer and flags. It may be
+ *   captured into a HIP graph (its epoch is counted on the device, as for ag_matmul_run).
  * Return codes as for ag_matmul_run. */
 int ag_gemm_ar_flags_create(int D, int64_t M, int64_t N, int64_t K_local, int dtype,
                             int block_m, agmm_handle** out_handle);

@@ -6,12 +6,15 @@ rewritten in place and another static call (another shape, which overwrites the 
 tables and flags) run eagerly before it, gives the handle path's output bit for bit, for the
 fused and baseline algorithms and both staging layouts.
 
-The runs whose kernels compare flags or split counters with a handle's run number (a fused
-handle, a handle with split tiles, the per-tile flag all-reduce) fix that number when they
-are enqueued, so they refuse a capturing stream with UNSUPPORTED and enqueue nothing; the
-handle then runs eagerly as before. A debug run, which synchronizes its stream, refuses it
-too. A baseline handle without split tiles compares nothing
-with a run number and may be captured and replayed.
+A handle's kernels take a run's epoch from the run counter in its workspace, which the last
+workgroup of every run advances, so a captured run of a handle replays correctly too, also
+interleaved with eager runs of the same handle on the same stream: fused runs in both
+layouts, runs with split tiles (whose piece counters are epoch-valued), the gathered-A run
+and the per-tile flag all-reduce. Every replay and every eager run must give the eager
+output bit for bit, and after all of them every staged unit's flag must equal the number of
+runs the device executed. A debug run (it synchronizes its stream) and a fetch-kernel run
+(it orders a stream of the handle's with events) refuse a capturing stream with UNSUPPORTED
+and enqueue nothing.
 """
 import ctypes
 
@@ -19,7 +22,8 @@ import numpy as np
 import pytest
 
 from agmm_testlib import assert_close, oracle_full, out_bits, run_gpu
-from workloads import Workload, make_inputs
+import oracle
+from workloads import Workload, bits, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -114,13 +118,141 @@ def test_static_run_captured_and_replayed(w, algo):
     del g
 
 
-def _raw_run(A, op, dev, out, stream):
-    return A.ag_matmul_run(op.handle, [t.data_ptr() for t in dev.shards], dev.B.data_ptr(),
-                           dev.bias.data_ptr() if dev.bias is not None else None,
-                           out.data_ptr(), stream)
+def _raw_run(A, op, dev, out, stream, a_out=None):
+    ptrs = [t.data_ptr() for t in dev.shards]
+    bias = dev.bias.data_ptr() if dev.bias is not None else None
+    if a_out is not None:
+        return A.ag_matmul_run_gather(op.handle, ptrs, dev.B.data_ptr(), bias, out.data_ptr(),
+                                      a_out.data_ptr(), stream)
+    return A.ag_matmul_run(op.handle, ptrs, dev.B.data_ptr(), bias, out.data_ptr(), stream)
 
 
-def test_epoch_runs_refuse_capture():
+HANDLES = [
+    # (name, workload, tunables)
+    ("fused_m", Workload("graph_h_m", 2, 2 * 544, 1024, 2048, "f16", "normal_sqrtk", True,
+                         "m_contiguous", True, 96, rank=1), dict(block_m=64)),
+    ("fused_k", Workload("graph_h_k", 4, 4 * 200, 328, 1032, "bf16", "normal_sqrtk", True,
+                         "k_contiguous", True, 97, rank=2), dict(block_m=128, k_per_flag=2)),
+    ("fused_split", Workload("graph_h_s", 2, 2 * 544, 1024, 2048, "f16", "normal_sqrtk", True,
+                             "m_contiguous", True, 98, rank=1),
+     dict(block_m=64, num_fetch_wgs=8, tail_split=1)),
+    ("baseline_split", Workload("graph_h_bs", 2, 2 * 544, 1024, 2048, "bf16", "normal_sqrtk",
+                                False, "k_contiguous", True, 99, rank=0),
+     dict(block_m=64, algo="baseline", tail_split=1)),
+    ("gather_a", Workload("graph_h_g", 4, 4 * 200, 328, 1032, "bf16", "normal_sqrtk", True,
+                          "k_contiguous", True, 100, rank=3), dict(gather_a=True)),
+]
+
+
+@pytest.mark.parametrize("name,w,tun", HANDLES, ids=[h[0] for h in HANDLES])
+def test_handle_run_captured_and_replayed(name, w, tun):
+    import torch
+    import all_gather_gemm_amd as A
+    from oracle import schedule_model as sm
+    print(f"case {name} {w.name} {tun}", flush=True)
+    tun = dict(tun)
+    algo = tun.pop("algo", "fused")
+    gather = tun.get("gather_a", False)
+    sets = [make_inputs(w, seed=w.seed + i) for i in range(2)]
+    srcs = [s.to("cuda") for s in sets]
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, algo=algo, rank=w.rank,
+                    has_bias=w.has_bias, **tun)
+    cfg = op.config.as_dict()
+    if "tail_split" in tun:
+        assert cfg["split_tiles"] > 0
+    td = w.torch_dtype()
+    out = torch.empty((w.M, w.N), dtype=td, device="cuda")
+    a_out = torch.empty((w.M, w.K), dtype=td, device="cuda") if gather else None
+    stream = lambda: torch.cuda.current_stream().cuda_stream
+    # eager references, each set run twice (runs 1 .. 4)
+    refs = []
+    for i in (0, 1, 0, 1):
+        assert _raw_run(A, op, srcs[i], out, stream(), a_out) == 0
+        torch.cuda.synchronize()
+        b = out_bits(out)
+        if len(refs) < 2:
+            refs.append(b)
+        assert np.array_equal(b, refs[i]), (name, "eager", i)
+    runs = 4
+    dev = sets[0].to("cuda")   # the buffers the graph reads
+    g = torch.cuda.CUDAGraph()
+    rcs = []
+    with torch.cuda.graph(g):
+        rcs.append(_raw_run(A, op, dev, out, stream(), a_out))
+    assert rcs == [0]
+    # replays, eager runs of the same handle between them
+    for it in range(6):
+        i = it % 2
+        _copy_into(dev, srcs[i])
+        out.fill_(float("nan"))
+        g.replay()
+        runs += 1
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), refs[i]), (name, "replay", it)
+        if gather:
+            assert np.array_equal(out_bits(a_out).reshape(w.M, w.K),
+                                  oracle.all_gather([bits(x) for x in sets[i].shards])), it
+        if it % 2 == 1:
+            j = 1 - i
+            out.fill_(float("nan"))
+            assert _raw_run(A, op, srcs[j], out, stream(), a_out) == 0
+            runs += 1
+            torch.cuda.synchronize()
+            assert np.array_equal(out_bits(out), refs[j]), (name, "eager between", it)
+    assert op.sync_status() == 0
+    if algo == "fused" and cfg["num_units"] > 0:
+        geo = sm.Geometry(w.D, w.M, w.N, w.K, cfg["block_m"], cfg["block_n"], cfg["block_k"],
+                          cfg["k_per_flag"], w.rank, True, cfg["num_fetch_wgs"],
+                          cfg["num_wgs"], num_cus=cfg["num_cus"], gather_a=gather)
+        assert np.array_equal(op.flags(), sm.expected_flags(geo, runs)), name
+    if name == "fused_m":
+        C, _ = oracle_full(w, sets[0])
+        _copy_into(dev, srcs[0])
+        g.replay()
+        torch.cuda.synchronize()
+        assert_close(w, out_bits(out), C, "handle, replayed")
+    del g
+    op.close()
+
+
+def test_allreduce_flags_captured_and_replayed():
+    """The per-tile flag all-reduce captured and replayed between eager runs: bit-identical
+    to the eager run every time (its result does not depend on timing)."""
+    import torch
+    import all_gather_gemm_amd as A
+    D, M, N, Kl = 3, 320, 264, 192
+    gen = torch.Generator().manual_seed(95)
+    Ap = [(torch.randn(M, Kl, generator=gen) / 8).half().cuda() for _ in range(D)]
+    Bp = [(torch.randn(Kl, N, generator=gen) / 8).half().cuda() for _ in range(D)]
+    bias = torch.randn(N, generator=gen).half().cuda()
+    h = A.GemmAllReduceFlags(D, M, N, Kl, block_m=64)
+    o = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    h.run(Ap, Bp, bias, out=o)
+    torch.cuda.synchronize()
+    ref = out_bits(o)
+    ap = (ctypes.c_void_p * D)(*[ctypes.c_void_p(t.data_ptr()) for t in Ap])
+    bp = (ctypes.c_void_p * D)(*[ctypes.c_void_p(t.data_ptr()) for t in Bp])
+    g = torch.cuda.CUDAGraph()
+    rcs = []
+    with torch.cuda.graph(g):
+        rcs.append(A.lib.ag_gemm_ar_flags_run(
+            ctypes.c_void_p(h.handle), ap, bp, ctypes.c_void_p(bias.data_ptr()),
+            ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    assert rcs == [0]
+    for it in range(4):
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(o), ref), ("replay", it)
+        o.fill_(float("nan"))
+        h.run(Ap, Bp, bias, out=o)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(o), ref), ("eager", it)
+    del g
+    h.close()
+
+
+def test_debug_and_fetch_kernel_runs_refuse_capture():
     import torch
     import all_gather_gemm_amd as A
     w = Workload("graph_refuse", 2, 2 * 544, 1024, 2048, "f16", "normal_sqrtk", True,
@@ -130,25 +262,17 @@ def test_epoch_runs_refuse_capture():
     dev = inp.to("cuda")
     plain = out_bits(run_gpu(w, inp, "baseline", dev_inp=dev, block_m=64).out)
     handles = {
-        "fused": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
-                            block_m=64),
-        "split": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
-                            block_m=64, algo="baseline", tail_split=1),
         "fetch_kernel": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank,
                                    has_bias=True, block_m=64, fetch_kernel=1),
-        # a debug run synchronizes its stream
         "debug": A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
-                            block_m=64, algo="baseline", debug=True),
+                            block_m=64, debug=True),
     }
-    assert handles["split"].config.split_tiles > 0
     out = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
     for name, op in handles.items():
         print(f"  handle {name}", flush=True)
         op.run(dev.shards, dev.B, dev.bias, out=out)   # one eager run first
         torch.cuda.synchronize()
-        ref = out_bits(out)
-        if name != "split":   # split tiles sum their K pieces in another order
-            assert np.array_equal(ref, plain), name
+        assert np.array_equal(out_bits(out), plain), name
         g = torch.cuda.CUDAGraph()
         rcs = []
         with torch.cuda.graph(g):
@@ -160,49 +284,6 @@ def test_epoch_runs_refuse_capture():
             out.fill_(float("nan"))
             op.run(dev.shards, dev.B, dev.bias, out=out)
             torch.cuda.synchronize()
-            assert np.array_equal(out_bits(out), ref), name
+            assert np.array_equal(out_bits(out), plain), name
         assert op.sync_status() == 0
         op.close()
-
-    # the per-tile flag all-reduce: refused the same way
-    D, M, N, Kl = 2, 128, 256, 192
-    gen = torch.Generator().manual_seed(95)
-    Ap = [torch.randn(M, Kl, generator=gen).half().cuda() for _ in range(D)]
-    Bp = [torch.randn(Kl, N, generator=gen).half().cuda() for _ in range(D)]
-    h = A.GemmAllReduceFlags(D, M, N, Kl)
-    r0 = out_bits(h.run(Ap, Bp))
-    torch.cuda.synchronize()
-    o = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    ap = (ctypes.c_void_p * D)(*[ctypes.c_void_p(t.data_ptr()) for t in Ap])
-    bp = (ctypes.c_void_p * D)(*[ctypes.c_void_p(t.data_ptr()) for t in Bp])
-    g = torch.cuda.CUDAGraph()
-    rcs = []
-    with torch.cuda.graph(g):
-        rcs.append(A.lib.ag_gemm_ar_flags_run(
-            ctypes.c_void_p(h.handle), ap, bp, None, ctypes.c_void_p(o.data_ptr()),
-            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
-    assert rcs == [UNSUPPORTED]
-    del g
-    o2 = h.run(Ap, Bp)
-    torch.cuda.synchronize()
-    assert np.array_equal(out_bits(o2), r0)
-    h.close()
-
-    # a baseline handle without split tiles compares nothing with a run number: captured,
-    # its replays match the eager run
-    op = A.AgMatmul(w.D, w.M, w.N, w.K, layout=w.layout, rank=w.rank, has_bias=True,
-                    block_m=64, algo="baseline")
-    assert op.config.split_tiles == 0
-    op.run(dev.shards, dev.B, dev.bias, out=out)
-    g = torch.cuda.CUDAGraph()
-    rcs = []
-    with torch.cuda.graph(g):
-        rcs.append(_raw_run(A, op, dev, out, torch.cuda.current_stream().cuda_stream))
-    assert rcs == [0]
-    for _ in range(3):
-        out.fill_(float("nan"))
-        g.replay()
-        torch.cuda.synchronize()
-        assert np.array_equal(out_bits(out), plain)
-    del g
-    op.close()
