@@ -408,6 +408,49 @@ def mfma_ceiling(torch, A, iters=20000):
     return res
 
 
+def graph_replay(w, torch, A, runs=20, reps=5, **tun):
+    """Per-run time of `runs` fused runs issued from the host one by one (each through the
+    Python binding and the C ABI) against the same runs captured once into a HIP graph and
+    replayed: wall clock from the first enqueue to the end of the stream work, best of `reps`.
+    The kernels count run epochs on the device, so a captured run replays correctly."""
+    import time
+    from workloads import make_inputs
+    dev = make_inputs(w).to("cuda")
+    out = torch.empty((w.M, w.N), dtype=w.torch_dtype(), device="cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=w.layout, rank=w.rank,
+                    direct_local=w.direct_local, has_bias=w.has_bias, **tun)
+    run = lambda: op.run(dev.shards, dev.B, dev.bias, out=out)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+
+    def wall(fn):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) * 1e3 / runs
+            best = dt if best is None else min(best, dt)
+        return best
+
+    eager = wall(lambda: [run() for _ in range(runs)])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(runs):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, ref))
+    replay = wall(g.replay)
+    del g
+    op.close()
+    return {"workload": w.name, "runs": runs, "eager_ms_per_run": round(eager, 5),
+            "graph_ms_per_run": round(replay, 5), "graph_output_bit_identical": same}
+
+
 def timeline(w, torch, A, runs=3, **tun):
     """Fetch-vs-GEMM overlap of the fused kernel from its debug trace (per-workgroup fetch,
     tile and wait records, 100 MHz timestamps) on the last of `runs` runs. Debug runs record
@@ -525,6 +568,10 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the MFMA rate with pseudo-random register operands (no "
                          "memory traffic), one set or four rotating, on 64, 256 and 512 workgroups")
+    ap.add_argument("--graph", action="store_true",
+                    help="only time fused runs issued one by one against the same runs captured "
+                         "in a HIP graph and replayed (for each of --workload, or of all five "
+                         "workloads with --sweep)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the "
                          "known-size reference for the HBM byte counters")
@@ -560,6 +607,10 @@ def main():
     if args.timeline:
         for w in (WORKLOADS if args.sweep else [BY_NAME[args.workload]]):
             print(json.dumps(timeline(w, torch, A)), flush=True)
+        return
+    if args.graph:
+        for w in (WORKLOADS if args.sweep else [BY_NAME[args.workload]]):
+            print(json.dumps(graph_replay(w, torch, A)), flush=True)
         return
     tun = {}
     if args.block_m:
