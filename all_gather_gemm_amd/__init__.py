@@ -40,7 +40,7 @@ EXPORTED = [
     "ag_matmul_run_gather", "ag_matmul_plan_query", "ag_gemm_ar_create", "ag_gemm_ar_run",
     "ag_gemm_ar_finalize", "ag_gemm_ar_flags_create", "ag_gemm_ar_flags_run",
     "ag_gemm_ar_flags_plan", "ag_matmul_sync_status", "ag_matmul_run_static",
-    "ag_matmul_debug_run_part", "ag_matmul_debug_mfma_loop",
+    "ag_matmul_debug_run_part", "ag_matmul_debug_mfma_loop", "ag_matmul_debug_set_runs",
 ]
 PART_COPY, PART_GEMM = 1, 2
 
@@ -146,6 +146,7 @@ def _load():
     lib.ag_matmul_get_config.argtypes = [vp, ctypes.POINTER(agmm_config)]
     lib.ag_matmul_debug_query.argtypes = [vp, ctypes.c_int, vp, ctypes.c_size_t]
     lib.ag_matmul_debug_fill_staging.argtypes = [vp, ctypes.c_uint16, vp]
+    lib.ag_matmul_debug_set_runs.argtypes = [vp, ctypes.c_uint32, vp]
     return lib
 
 
@@ -279,6 +280,11 @@ def ag_matmul_debug_query(handle: int, what: int, nbytes: int) -> bytes:
     if rc != AGMM_OK:
         raise AgmmError(rc, "ag_matmul_debug_query")
     return bytes(buf)[:nbytes]
+
+
+def ag_matmul_debug_set_runs(handle: int, runs: int, stream: int = 0) -> int:
+    return lib.ag_matmul_debug_set_runs(ctypes.c_void_p(handle), runs & 0xFFFFFFFF,
+                                        ctypes.c_void_p(stream))
 
 
 def ag_matmul_debug_fill_staging(handle: int, pattern: int, stream: int = 0) -> int:
@@ -443,6 +449,15 @@ class AgMatmul:
                                                    W * c.trace_cap * TRACE_DTYPE.itemsize),
                              dtype=TRACE_DTYPE).reshape(W, c.trace_cap)
         return counts, recs
+
+    def set_runs(self, runs: int, stream=None):
+        """Test knob: put the flags, split counters and device run counter where `runs` runs
+        would have left them (ag_matmul_debug_set_runs)."""
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = ag_matmul_debug_set_runs(self.handle, runs, s.cuda_stream)
+        if rc != AGMM_OK:
+            raise AgmmError(rc, "ag_matmul_debug_set_runs")
 
     def fill_staging(self, pattern: int, stream=None):
         import torch

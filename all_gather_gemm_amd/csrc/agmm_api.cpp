@@ -1323,6 +1323,28 @@ int ag_matmul_debug_mfma_loop(int dtype, int vary, int grid, int iters, float* s
   return AGMM_OK;
 }
 
+int ag_matmul_debug_set_runs(agmm_handle* h, uint32_t runs, void* hip_stream) {
+  if (!h || h->desc.algo == AGMM_ALGO_PIPELINED || (h->ar_D && !h->ar_flags_mode))
+    return AGMM_ERR_INVALID_ARG;
+  if (h->poisoned) return AGMM_ERR_POISONED;
+  int cur = 0;
+  AGMM_HIP(hipGetDevice(&cur));
+  if (cur != h->cfg.device) return AGMM_ERR_WRONG_DEVICE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  // the state `runs` runs leave: every flag at the last run's epoch (the per-tile flag
+  // variant stores it, the fetch adds one per run), every split counter at pieces per run,
+  // and the run counter
+  if (h->ar_flags_mode) {
+    AGMM_HIP(agmm::launch_fill32(h->ar_flags, h->ar_flags_n, runs, s));
+  } else {
+    AGMM_HIP(agmm::launch_fill32(h->flags, h->flags_n, runs, s));
+    AGMM_HIP(agmm::launch_fill32(h->split_cnt, h->cfg.split_tiles,
+                                 runs * (uint32_t)h->cfg.split_pieces, s));
+  }
+  AGMM_HIP(agmm::launch_fill32(h->ctr + agmm::CTR_RUNS, 1, runs, s));
+  return AGMM_OK;
+}
+
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream) {
   if (!h) return AGMM_ERR_INVALID_ARG;
   int cur = 0;

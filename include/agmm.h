@@ -407,6 +407,16 @@ int ag_matmul_plan_query(const agmm_desc* desc, int num_cus, int what, void* dst
  * staging) on `hip_stream`. */
 int ag_matmul_debug_fill_staging(agmm_handle* h, uint16_t pattern, void* hip_stream);
 
+/* Test knob for the run count (mod 2^32) that the kernels keep on the device: enqueues on
+ * `hip_stream` fill kernels that put the handle's flags, split counters and run counter
+ * where `runs` runs would have left them. Every flag is set to `runs` (staged units' flags
+ * equal the run count, and the per-tile flag variant stores the epoch), and every split
+ * counter to runs * split_pieces. The next run then has epoch runs + 1, so runs near 2^32
+ * test the wrap-around. Plain, baseline and per-tile flag all-reduce handles; INVALID_ARG
+ * for pipelined and atomics all-reduce handles. Returns AGMM_OK, INVALID_ARG, POISONED,
+ * WRONG_DEVICE or HIP. */
+int ag_matmul_debug_set_runs(agmm_handle* h, uint32_t runs, void* hip_stream);
+
 /* Measurement of the barrier baseline's two phases on their own: for a handle with
  * algo = AGMM_ALGO_BASELINE (and no gather_a), enqueues only the staging copy
  * (AGMM_PART_COPY: every staged unit of A into the staging buffer, [M][K]) or only the GEMM
