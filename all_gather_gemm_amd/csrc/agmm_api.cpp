@@ -81,6 +81,7 @@ constexpr int64_t kMaxDimNK = (int64_t)1 << 22;
 constexpr int64_t kMaxCount = (int64_t)1 << 31;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;  // ~ several seconds of backed-off polls
 constexpr int kDefaultTraceCap = 512;
+constexpr uint16_t kNanF16 = 0x7E00, kNanBF16 = 0x7FC0;  // quiet NaNs: debug staging poison
 constexpr int kTraceWgsAuto = 2048;
 constexpr int kDefaultFetchWgs = 32;  // the iris issue's tuned num_fetch_sms default
 constexpr int kDefaultChunks = 4;     // AGMM_ALGO_PIPELINED: chunks per shard
@@ -865,6 +866,11 @@ int run_impl(agmm_handle* h, const void* const* shards, const void* B, const voi
 
   KParams p = run_params(h, shards, B, bias, out,
                           d.gather_a ? static_cast<uint16_t*>(a_gathered) : h->staging);
+  // debug: the staging buffer holds a quiet NaN everywhere before the run, so a tile that
+  // read a staged unit before it was written would put NaN into the output
+  if (d.debug && c.staging_elems > 0)
+    AGMM_HIP(agmm::launch_fill16(h->staging, c.staging_elems,
+                                 d.dtype == AGMM_BF16 ? kNanBF16 : kNanF16, s));
 
   if (d.algo == AGMM_ALGO_FUSED && c.fetch_kernel) {
     // The fetch kernel on the handle's stream, after the caller's stream reaches this point;

@@ -82,7 +82,9 @@ typedef struct agmm_desc {
   int32_t algo;          /* AGMM_ALGO_FUSED, AGMM_ALGO_BASELINE or AGMM_ALGO_PIPELINED */
   int32_t direct_local;  /* 1: local-shard tiles read in place; 0: every tile staged */
   int32_t has_bias;      /* 1: run() takes a bias[N] pointer; 0: bias must be NULL */
-  int32_t debug;         /* 1: record per-workgroup trace; run() synchronizes and reports
+  int32_t debug;         /* 1: record per-workgroup trace; fill the staging buffer with a
+                            quiet NaN before every run (so a read of unwritten staging shows
+                            in the output); run() synchronizes and reports
                             a flag-wait timeout as AGMM_ERR_TIMEOUT */
   int32_t block_m;       /* output tile edge: 64, 128 or 256 (tile is square); 0 = auto: the
                             largest with at least 3/4 of a tile per CU; fused, 128 instead

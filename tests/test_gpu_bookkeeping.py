@@ -116,6 +116,45 @@ def test_bookkeeping_matches_model(w, bm, kpf, nf):
     op.close()
 
 
+@pytest.mark.parametrize("algo,layout", [("fused", "m_contiguous"), ("fused", "k_contiguous"),
+                                         ("baseline", "k_contiguous")])
+def test_debug_run_poisons_staging(algo, layout):
+    """A debug run fills the staging buffer with the type's quiet NaN before its kernels
+    run: after a run that follows an explicit fill with 1.0, every staging element the run
+    does not write holds the NaN, and the staged ones hold A, as the model has them."""
+    import torch
+    import all_gather_gemm_amd as A
+    w = Workload(f"poison_{algo}_{layout}", 4, 4 * 256, 512, 1024, "bf16", "normal_sqrtk",
+                 True, layout, True, 36, rank=1)
+    print(f"case {w.name}", flush=True)
+    inp = make_inputs(w)
+    g_in = inp.to("cuda")
+    op = A.AgMatmul(w.D, w.M, w.N, w.K, dtype=w.dtype, layout=layout, algo=algo, rank=w.rank,
+                    has_bias=True, debug=True, block_m=128)
+    cfg = op.config.as_dict()
+    op.fill_staging(0x3F80)  # bf16 1.0
+    out = op.run(g_in.shards, g_in.B, g_in.bias)
+    torch.cuda.synchronize()
+    C, _ = oracle_full(w, inp)
+    import oracle
+    assert oracle.check(w.dtype, out_bits(out), C)["bad"] == 0
+    st = op.staging()
+    A_bits = np.concatenate([bits(s) for s in inp.shards])
+    if algo == "fused":
+        g = geometry(w, cfg)
+        exp = sm.expected_staging(g, A_bits, layout, NAN16[w.dtype])
+    else:  # the baseline stages every non-local row, [M][K]
+        exp = np.full((w.M, w.K), NAN16[w.dtype], dtype=np.uint16)
+        for d in range(w.D):
+            if d != w.rank:
+                exp[d * w.M_s:(d + 1) * w.M_s] = A_bits.reshape(w.M, w.K)[d * w.M_s:(d + 1) * w.M_s]
+        exp = exp.reshape(-1)
+    assert np.array_equal(st, exp)
+    assert (st == NAN16[w.dtype]).any()   # the local rows are never written
+    assert not (st == 0x3F80).any()
+    op.close()
+
+
 def test_alternating_inputs_and_poisoned_staging():
     """Two input sets alternate while staging is re-poisoned each run: a read of stale or
     unwritten staging would show up as a mismatch against the baseline output."""
