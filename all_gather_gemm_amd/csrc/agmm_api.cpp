@@ -227,12 +227,15 @@ int make_plan(const agmm_desc& d, int num_cus, Plan* pl) {
   // arrives, and a smaller first group arrives sooner; with short K, finer groups catch up
   // with the fetch front and cost more acquires than they save.
   // The 128-row fused case above takes 512 columns too: twice the units, so twice the
-  // fetchers, each done in half the time. A long-K grid that runs in one round beside the
-  // default fetchers (4096x3584x8192 with 4 shards) takes 256: its tiles then start on
-  // half the first k-group (1-3% faster there).
+  // fetchers, each done in half the time. A long-K grid of 256-row tiles that runs in one
+  // round beside the default fetchers (4096x3584x8192 with 4 or 8 shards) takes 256: its
+  // tiles then start on half the first k-group (1-3% faster there). One-round grids of
+  // 128-row tiles keep 512 (1024x3584x8192 with 2 to 8 shards: 2-5% faster than with 256,
+  // whose twice as many k-groups cost the short tiles more acquires than they save).
   int kg_cols = (d.K >= 4096 || fused_128) ? 512 : 1024;
   const int64_t W_cap = std::min<int64_t>(d.num_wgs ? d.num_wgs : num_cus, num_cus);
-  if (d.algo == AGMM_ALGO_FUSED && d.K >= 4096 && T_m * T_n + kDefaultFetchWgs <= W_cap)
+  if (d.algo == AGMM_ALGO_FUSED && d.K >= 4096 && bm == 256 &&
+      T_m * T_n + kDefaultFetchWgs <= W_cap)
     kg_cols = 256;
   c.k_per_flag = d.k_per_flag ? d.k_per_flag : std::max(1, kg_cols / c.block_k);
   const int64_t KG = (int64_t)c.k_per_flag * c.block_k;

@@ -92,8 +92,8 @@ typedef struct agmm_desc {
                             fetchers and 128-row tiles still give a quarter of the CUs one */
   int32_t k_per_flag;    /* K-tiles covered by one ready flag; 0 = auto: 512 columns when
                             K >= 4096 or in the fused 128-row case above, else 1024; fused
-                            with K >= 4096 and every tile in one round beside 32 spare
-                            workgroups, 256 */
+                            with K >= 4096, 256-row tiles and every tile in one round beside
+                            32 spare workgroups, 256 */
   int32_t num_fetch_wgs; /* fetcher workgroups (fused); 0 = auto: 32, or one per fetch unit
                             when all tiles fit in one round with fewer than 32 workgroups
                             to spare */
