@@ -169,3 +169,24 @@ def test_one_hip_runtime_whatever_the_import_order():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))), timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip() == "1", r.stdout
+
+
+def test_planner_defaults_at_the_measured_shapes(A):
+    """The planner's automatic choices at the shapes whose timings chose them (256 compute
+    units, fp16, N = 3584, K = 8192): tile rows, k-group size in K-tiles of 32, fetchers, wait
+    mode."""
+    def cfg(**kw):
+        return A.ag_matmul_plan_query(A.ag_matmul_desc_init(N=3584, K=8192, **kw), 256)["config"]
+    # 16384 rows, 8 shards: 256-row tiles, k-groups of 512 columns, 32 fetchers, per-k-group waits
+    c = cfg(D=8, M=16384, layout=A.M_CONTIGUOUS, has_bias=1)
+    assert (c.block_m, c.k_per_flag, c.num_fetch_wgs, c.row_wait) == (256, 16, 32, 0)
+    # 4096 rows, 4 shards: one round of 224 tiles beside 32 fetchers, k-groups of 256 columns
+    c = cfg(D=4, M=4096)
+    assert (c.block_m, c.k_per_flag, c.num_fetch_wgs, c.num_tiles) == (256, 8, 32, 224)
+    # 1024 rows: one round of 224 tiles of 128 rows, k-groups of 512 columns
+    for D in (2, 4, 8):
+        c = cfg(D=D, M=1024)
+        assert (c.block_m, c.k_per_flag, c.num_fetch_wgs, c.num_tiles) == (128, 16, 32, 224), D
+    # the baseline's copy units follow the same k-groups (512 columns once K >= 4096)
+    c = cfg(D=8, M=16384, algo=A.ALGO_BASELINE)
+    assert c.k_per_flag == 16
