@@ -490,9 +490,10 @@ bool timed_out(agmm_handle* h) {
 }
 
 // Runs that a captured graph could not replay refuse a capturing stream: a debug run
-// synchronizes the stream, and a fetch-kernel run orders a second stream of the handle's
-// with events. (The kernels count runs on the device, so a fused run itself replays
-// correctly.)
+// synchronizes the stream, and a fetch-kernel run's GEMM grid waits on flags that only the
+// fetch kernel beside it sets, which a graph may run after it instead. (The kernels count
+// runs on the device, so a fused run itself replays correctly, and a pipelined run's chunk
+// streams join the capture through its events.)
 int refuse_capture(hipStream_t s) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   AGMM_HIP(hipStreamIsCapturing(s, &cs));

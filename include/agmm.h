@@ -218,10 +218,12 @@ int ag_matmul_create(const agmm_desc* desc, void* workspace, size_t workspace_by
  * Graph capture: the run's kernels take its epoch (the value its flags and split counters
  * must reach) from a run counter in the workspace, which the last workgroup of every run
  * advances. A run may therefore be captured into a HIP graph, and the graph replayed any
- * number of times, interleaved with eager runs of the same handle on the same stream. Two
- * kinds of run return UNSUPPORTED on a capturing stream and enqueue nothing: a debug run,
- * which synchronizes the stream, and a fetch_kernel = 1 run, which orders a stream of the
- * handle's with events.
+ * number of times, interleaved with eager runs of the same handle on the same stream. A
+ * pipelined run's chunk streams join the capture through its events. Two kinds of run
+ * return UNSUPPORTED on a capturing stream and enqueue nothing: a debug run, which
+ * synchronizes the stream, and a fetch_kernel = 1 run, whose GEMM grid waits on flags that
+ * only the fetch kernel running beside it sets (a graph may run the two one after the
+ * other).
  * Returns AGMM_OK, INVALID_ARG (also for a gather_a handle), WRONG_DEVICE, POISONED, HIP,
  * UNSUPPORTED (capture, above), or TIMEOUT. A flag wait that exceeds the spin limit makes
  * every workgroup of the launch stop early (the output is then incomplete); the launch's last

@@ -9,8 +9,9 @@ fused and baseline algorithms and both staging layouts.
 A handle's kernels take a run's epoch from the run counter in its workspace, which the last
 workgroup of every run advances, so a captured run of a handle replays correctly too, also
 interleaved with eager runs of the same handle on the same stream: fused runs in both
-layouts, runs with split tiles (whose piece counters are epoch-valued), the gathered-A run
-and the per-tile flag all-reduce. Every replay and every eager run must give the eager
+layouts, runs with split tiles (whose piece counters are epoch-valued), the gathered-A run,
+the host pipeline (its chunk streams join the capture through its events) and the per-tile
+flag all-reduce. Every replay and every eager run must give the eager
 output bit for bit, and after all of them every staged unit's flag must equal the number of
 runs the device executed. A debug run (it synchronizes its stream) and a fetch-kernel run
 (it orders a stream of the handle's with events) refuse a capturing stream with UNSUPPORTED
@@ -141,6 +142,10 @@ HANDLES = [
      dict(block_m=64, algo="baseline", tail_split=1)),
     ("gather_a", Workload("graph_h_g", 4, 4 * 200, 328, 1032, "bf16", "normal_sqrtk", True,
                           "k_contiguous", True, 100, rank=3), dict(gather_a=True)),
+    # the host stream pipeline: its chunk streams join the capture through its events
+    ("pipelined", Workload("graph_h_p", 4, 4 * 256, 392, 520, "f16", "normal_sqrtk", True,
+                           "k_contiguous", True, 101, rank=2),
+     dict(block_m=64, algo="pipelined", pipeline_chunks=4)),
 ]
 
 
