@@ -335,22 +335,25 @@ def standalone_ops(w, A, tun):
             ("fetch_kernel", mk("fused", fetch_kernel=1))]
 
 
-def cold_times(op, dev, torch, reps, flush_bytes=1 << 30):
-    """ms of single runs, each after 1 GiB of unrelated writes (untimed) have pushed the
-    op's working set out of the caches."""
+def cold_times(ops, dev, torch, reps, flush_bytes=1 << 30):
+    """Median ms of single runs of each op, each run after 1 GiB of unrelated writes (untimed)
+    have pushed the op's working set out of the caches. The ops take turns, so that the
+    clock's drift over the series (the first runs after a pause are slow) falls on all of
+    them alike."""
     junk = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
-    per = []
-    for _ in range(reps):
-        junk.fill_(7)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
-        e1.record()
-        torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1))
+    per = {n: [] for n, _ in ops}
+    for i in range(reps):
+        for n, op in (ops if i % 2 == 0 else ops[::-1]):
+            junk.fill_(7)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
+            e1.record()
+            torch.cuda.synchronize()
+            per[n].append(e0.elapsed_time(e1))
     del junk
     torch.cuda.empty_cache()
-    return statistics.median(per)
+    return {n: statistics.median(v) for n, v in per.items()}
 
 
 def baseline_parts(w, dev, torch, A, reps=20):
@@ -719,12 +722,13 @@ def main():
         if args.algo == "fused":
             bops = standalone_ops(w, A, tun)
             bt = block_times(w, bops, r["dev"], torch, 6, 10)
+            ct = cold_times(bops[:2], r["dev"], torch, 10)
             res["standalone"] = {"fused_ms": round(bt["fused"], 5),
                                  "baseline_ms": round(bt["baseline"], 5),
                                  "fused_speedup": round(bt["baseline"] / bt["fused"], 3),
                                  "fetch_kernel_ms": round(bt["fetch_kernel"], 5),
-                                 "cold_fused_ms": round(cold_times(bops[0][1], r["dev"], torch, 10), 5),
-                                 "cold_baseline_ms": round(cold_times(bops[1][1], r["dev"], torch, 10), 5)}
+                                 "cold_fused_ms": round(ct["fused"], 5),
+                                 "cold_baseline_ms": round(ct["baseline"], 5)}
             res["clock"] = clock_under_load(bops[0][1], r["dev"], torch)
             for _, op in bops:
                 op.close()
