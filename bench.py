@@ -9,17 +9,17 @@ every launch on the launch stream (the fused path is one kernel per step, so the
 time that kernel). TFLOP/s counts 2*M*N*K per step with M the full gathered row count, the
 convention of the iris issue's results tables.
 
-Prints ONE JSON line on stdout. Unless --no-extras, the line also carries the other
-variants on the same inputs: the copy-barrier-GEMM baseline (runs interleaved with the fused
-ones, and "standalone": each timed back to back in alternating blocks, plus cold-cache
-single runs, each after 1 GiB of unrelated writes, the two handles taking turns), the
-baseline's copy and GEMM phases timed alone (the copy's staging rate against the HBM
-peak), the shader clock sampled under sustained fused load, the host stream pipeline (2,
-4, 8 chunks), the variant that also returns the gathered A, the GEMM + all-reduce variants, and torch.matmul on a pre-gathered A as a
-yardstick. kernel_resources gives the fused and GEMM kernels' registers, spills and LDS from
-the built code object. `--sweep` additionally writes a table of all five workloads to stderr
-and, with --out, to a JSON-lines file; `--timeline` prints the fused kernel's fetch/GEMM
-overlap from a debug trace instead.
+Prints ONE JSON line on stdout. Unless --no-extras, the line also carries the other variants
+on the same inputs: the copy-barrier-GEMM baseline (runs interleaved with the fused ones,
+and "standalone": each timed back to back in alternating blocks, plus cold-cache single
+runs, each after 1 GiB of unrelated writes, the two handles taking turns), the baseline's
+copy and GEMM phases timed alone (the copy's staging rate against the HBM peak), the shader
+clock sampled under sustained fused load, the host stream pipeline (2, 4, 8 chunks), the
+variant that also returns the gathered A, the GEMM + all-reduce variants, and torch.matmul
+on a pre-gathered A as a yardstick. kernel_resources gives the fused and GEMM kernels'
+registers, spills and LDS from the built code object. `--sweep` additionally writes a table
+of all five workloads to stderr and, with --out, to a JSON-lines file; `--timeline` prints
+the fused kernel's fetch/GEMM overlap from a debug trace instead.
 """
 import argparse
 import json
