@@ -575,6 +575,10 @@ def main():
                     help="only time fused runs issued one by one against the same runs captured "
                          "in a HIP graph and replayed (for each of --workload, or of all five "
                          "workloads with --sweep)")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="only time torch.matmul (hipBLASLt) on a pre-gathered A of --workload: "
+                         "--warmup untimed and --steps timed launches, for counter runs beside "
+                         "the library's GEMM kernel")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the "
                          "known-size reference for the HBM byte counters")
@@ -614,6 +618,13 @@ def main():
     if args.graph:
         for w in (WORKLOADS if args.sweep else [BY_NAME[args.workload]]):
             print(json.dumps(graph_replay(w, torch, A)), flush=True)
+        return
+    if args.yardstick:
+        from workloads import make_inputs
+        w = BY_NAME[args.workload]
+        ms = yardstick_matmul(w, make_inputs(w).to("cuda"), args.steps, args.warmup, torch)
+        print(json.dumps({"workload": w.name, "yardstick_torch_matmul_pregathered_ms": round(ms, 5),
+                          "tflops": round(tflops(w.M, w.N, w.K, ms / 1e3), 3)}), flush=True)
         return
     tun = {}
     if args.block_m:
