@@ -22,6 +22,7 @@ of all five workloads to stderr and, with --out, to a JSON-lines file; `--timeli
 the fused kernel's fetch/GEMM overlap from a debug trace instead.
 """
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -638,7 +639,11 @@ def main():
 
     if args.sweep:
         rows = []
-        for w in WORKLOADS:
+        # the 4096^3 cube also with its own shard staged like the others (direct-local off),
+        # beside the default in-place read
+        cube = BY_NAME["square_4096_d8_bf16"]
+        extra = [dataclasses.replace(cube, name=cube.name + "_direct_local_off", direct_local=False)]
+        for w in list(WORKLOADS) + extra:
             med, cfgs, _, dev = interleaved(w, ("fused", "baseline", "pipelined"), args.steps,
                                             args.warmup, torch, A, **tun)
             ym = yardstick_matmul(w, dev, args.steps, args.warmup, torch)
