@@ -83,14 +83,17 @@ struct Num<AGMM_BF16> {
 // their source has in global memory, so both are copied global->LDS by buffer loads that
 // write LDS directly (no registers, no VALU):
 //  - a K-contiguous slice (A from a shard or k_contiguous staging) as [row][4 chunks], the
-//    chunk index XORed with g(row) = (row>>1 ^ row>>3) & 3; an MFMA operand is one 16-byte
-//    read per lane;
+//    chunk index XORed with g(row) = (row>>2) & 3; an MFMA operand is one 16-byte read per
+//    lane. The LDS serves a 16-byte read in passes of 16 lanes over 256 bytes (64 banks):
+//    the 16 rows of a pass then fill 16 distinct 16-byte slots (row%4 picks the 64-byte
+//    quarter, (row>>2)%4 the slot in it). Measured with SQ_LDS_BANK_CONFLICT: no conflict,
+//    where the earlier g(row) = (row>>1 ^ row>>3) & 3 cost 4 cycles per read;
 //  - an MN-contiguous slice (B, or A from m_contiguous staging) as [k][MN/8 chunks], the
 //    chunk index XORed with f(k) = 4*(k%4) (4*((k>>1)%2) when a row has 8 chunks); an MFMA
 //    operand is two transposing 8-byte reads (ds_read_b64_tr_b16) per lane.
 // Checked on the CPU against the instruction's lane mapping (measured on the hardware):
-// every MFMA lane receives its elements and no 16-lane or 32-lane read pass has a bank
-// conflict; each DMA instruction fills 1 KiB of LDS linearly.
+// every MFMA lane receives its elements; each DMA instruction fills 1 KiB of LDS linearly.
+// The transposing reads of the MN-contiguous slices show no bank conflicts in the counters.
 template <int BM_>
 struct Tile {
   static constexpr int BM = BM_, BN = BM_, BK = kBlockK, NKK = BK / 16;
@@ -111,7 +114,7 @@ struct Tile {
   static_assert((NS - 2) * DMA_PER_TILE + ADMA <= 63, "DMA requests within the counter");
 };
 
-__device__ inline int g_row(int m) { return ((m >> 1) ^ (m >> 3)) & 3; }
+__device__ inline int g_row(int m) { return (m >> 2) & 3; }
 template <int RC>
 __device__ inline int f_row(int k) { return RC >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 
