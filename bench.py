@@ -274,24 +274,35 @@ def measured_traffic(workload_name, algo):
 
 
 def sample_sclk(n=4, gap_s=0.3):
-    """Shader clock (MHz) read with rocm-smi n times, gap_s apart (None where unreadable)."""
+    """Shader clock (MHz, rocm-smi) and socket power (W, amd-smi), read n times gap_s apart
+    (None where unreadable)."""
     import re
     import subprocess
     out = []
     for i in range(n):
+        clk = pw = None
         try:
             r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
                                text=True, timeout=20)
             m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', r.stdout)
-            out.append(int(m.group(1)) if m else None)
+            clk = int(m.group(1)) if m else None
         except Exception:
-            out.append(None)
+            pass
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "--json"],
+                               capture_output=True, text=True, timeout=20)
+            m = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
+            pw = int(m.group(1)) if m else None
+        except Exception:
+            pass
+        out.append((clk, pw))
         time.sleep(gap_s)
     return out
 
 
 def clock_under_load(op, dev, torch, seconds=2.0):
-    """Median shader clock while the op runs back to back for about `seconds`."""
+    """Median shader clock and socket power while the op runs back to back for about
+    `seconds`."""
     import threading
     samples = []
     th = threading.Thread(target=lambda: samples.extend(sample_sclk(4, seconds / 6)))
@@ -302,8 +313,11 @@ def clock_under_load(op, dev, torch, seconds=2.0):
             op.run(dev.shards, dev.B, dev.bias, out=dev.out, check=False)
         torch.cuda.synchronize()
     th.join()
-    vals = sorted(v for v in samples if v)
-    return {"sclk_mhz_samples": samples, "sclk_mhz_median": vals[len(vals) // 2] if vals else None}
+    med = lambda v: sorted(v)[len(v) // 2] if v else None
+    clk = [c for c, _ in samples]
+    pw = [p for _, p in samples]
+    return {"sclk_mhz_samples": clk, "sclk_mhz_median": med([c for c in clk if c]),
+            "socket_power_w_samples": pw, "socket_power_w_median": med([p for p in pw if p])}
 
 
 def block_times(w, ops, dev, torch, blocks, per):
