@@ -14,12 +14,12 @@ on the same inputs: the copy-barrier-GEMM baseline (runs interleaved with the fu
 and "standalone": each timed back to back in alternating blocks, plus cold-cache single
 runs, each after 1 GiB of unrelated writes, the two handles taking turns), the baseline's
 copy and GEMM phases timed alone (the copy's staging rate against the HBM peak), the shader
-clock sampled under sustained fused load, the host stream pipeline (2, 4, 8 chunks), the
-variant that also returns the gathered A, the GEMM + all-reduce variants, and torch.matmul
-on a pre-gathered A as a yardstick. kernel_resources gives the fused and GEMM kernels'
-registers, spills and LDS from the built code object. `--sweep` additionally writes a table
-of all five workloads to stderr and, with --out, to a JSON-lines file; `--timeline` prints
-the fused kernel's fetch/GEMM overlap from a debug trace instead.
+clock and socket power sampled under sustained fused load, the host stream pipeline (2, 4, 8
+chunks), the variant that also returns the gathered A, the GEMM + all-reduce variants, and
+torch.matmul on a pre-gathered A as a yardstick. kernel_resources gives the fused and GEMM
+kernels' registers, spills and LDS from the built code object. `--sweep` additionally writes
+a table of all five workloads to stderr and, with --out, to a JSON-lines file; `--timeline`
+prints the fused kernel's fetch/GEMM overlap from a debug trace instead.
 """
 import argparse
 import dataclasses
